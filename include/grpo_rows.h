@@ -1,0 +1,234 @@
+/*
+ * grpo_rows.h -- C ABI of the MI355X (gfx950) row-wise GRPO logits library.
+ *
+ * The library computes, over LM-head logits laid out as N = B*L rows of V
+ * vocabulary entries, the per-row work of GRPO fine-tuning: a temperature-
+ * scaled log-sum-exp, the log-softmax of the sampled token, the entropy, the
+ * per-token GRPO loss (PPO clipped-ratio surrogate plus beta * k3 KL against a
+ * reference log-probability), and the backward
+ *     dlogits = dlogp * (onehot(y) - softmax(z / T)) / T
+ * with an all-zero, write-only path for rows whose dlogp is exactly 0.
+ * A chunked fused-linear entry point forms the logits of one batch chunk from
+ * hidden states and the LM-head weight, and accumulates the gradients of both
+ * during the forward, so the full logits are never held.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [LIGER-BWD] Liger-Kernel PR #1550 analysis, "GRPO loss backward
+ *               optimisation": "Code analysis" (the _grpo_loss_bwd_kernel and
+ *               _grpo_loss_bwd_kernel_seq hunks) and "Why is this good".
+ *   [LIGER-TRL] "Liger GRPO meets TRL" summary, detailed items 3 and 4.
+ *   [AXOLOTL]   axolotl PR #3510 analysis, "entropy and selective log-softmax
+ *               with Triton kernels", "Code analysis" parts 1 and 2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Ownership: every array argument is a DEVICE pointer owned by the caller.
+ *    The library never allocates, frees or copies device memory; the fused
+ *    path uses only the workspace the caller passes.  Parameter structs are
+ *    host pointers, read during the call only.
+ *  - Layout: logits are row-major [rows, ld] with row r at logits + r*ld
+ *    elements and the first V entries of each row used (ld >= V; a slice of a
+ *    wider buffer is allowed).  Row r of a GRPO batch is token t of sequence
+ *    b with r = b*L + t.  Per-row arrays are dense [B*L]; per-sequence arrays
+ *    are dense [B].
+ *  - dtype: GRPO_F32 (float) or GRPO_BF16 (bfloat16 bit patterns, uint16).
+ *    Arithmetic is fp32 with fp32 accumulation.  dlogits has the logits'
+ *    dtype; bf16 results are rounded to nearest even.
+ *  - Execution: all work is enqueued asynchronously on `stream` (a
+ *    hipStream_t; NULL is the default stream).  No call synchronises.
+ *  - Errors: argument errors are detected on the host and returned before
+ *    anything is enqueued (no device is touched).  A launch failure returns
+ *    GRPO_ERR_LAUNCH.  Data errors are not status codes (that would need a
+ *    sync): an id outside [0, V) makes that row's outputs NaN and, where an
+ *    err_count pointer is given, adds 1 to it with a device atomic.
+ *    NaN/Inf in the logits propagate to the outputs of their row.
+ *  - Alignment: pointers must be aligned to their element size.  Rows whose
+ *    byte address is 16-byte aligned take 128-bit loads and stores; other
+ *    layouts take an element-wise path with the same results.
+ *  - Aliasing: dlogits may alias logits only with the same dtype and
+ *    ld_out == ld (in place).  No other output may alias an input.
+ *  - Thread safety: stateless and reentrant.  rows == 0 is a no-op.
+ */
+#ifndef GRPO_ROWS_H
+#define GRPO_ROWS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum grpo_status {
+  GRPO_OK = 0,
+  GRPO_ERR_NULL = 1,      /* a required pointer is NULL                      */
+  GRPO_ERR_SHAPE = 2,     /* B, L, V, rows, H out of range                   */
+  GRPO_ERR_STRIDE = 3,    /* ld < V or ld_out < V                            */
+  GRPO_ERR_DTYPE = 4,     /* dtype not GRPO_F32 / GRPO_BF16                  */
+  GRPO_ERR_ALIGN = 5,     /* pointer not aligned to its element size         */
+  GRPO_ERR_WORKSPACE = 6, /* fused-linear workspace NULL or too small        */
+  GRPO_ERR_LAUNCH = 7,    /* the HIP runtime refused a launch                */
+  GRPO_ERR_PARAM = 8      /* temperature <= 0, eps out of range, bad level   */
+};
+
+enum grpo_dtype { GRPO_F32 = 0, GRPO_BF16 = 1 };
+enum grpo_level { GRPO_TOKEN = 0, GRPO_SEQUENCE = 1 };
+
+/* flags: GRPO_FLAG_FORCE_DENSE makes the backward take the dense path on every
+ * row (the all-zero path is skipped even when dlogp == 0); results are equal
+ * to the default up to the sign of zero.  Used to check the early path. */
+enum grpo_flags { GRPO_FLAG_FORCE_DENSE = 1u };
+
+/* Loss settings.  temperature T > 0 divides the logits before the softmax
+ * [LIGER-BWD, "Code analysis": division by TEMPERATURE].  beta >= 0 weighs the
+ * k3 KL term (beta = 0 drops it) [same passage: BETA].  The ratio is clipped
+ * to [1 - eps_low, 1 + eps_high] (0 <= eps_low < 1, eps_high >= 0).  level is
+ * GRPO_TOKEN (one ratio per token) or GRPO_SEQUENCE (one ratio per sequence,
+ * from the mask-weighted mean log-ratio) [LIGER-BWD: _grpo_loss_bwd_kernel
+ * and _grpo_loss_bwd_kernel_seq]. */
+typedef struct grpo_params {
+  float temperature;
+  float beta;
+  float eps_low;
+  float eps_high;
+  int32_t level;
+  uint32_t flags;
+} grpo_params;
+
+/* ------------------------------------------------------------------------
+ * grpo_logits_fwd -- forward row pass of the GRPO loss.
+ * Defines: per row r, u = z_r / T, lse = log sum_j e^{u_j},
+ *   logp = u_y - lse, entropy = -sum_j p_j log p_j, x = logp - old_logp,
+ *   ratio = e^x, pg = -min(ratio*A, clip(ratio, 1-eps_low, 1+eps_high)*A),
+ *   kl = e^d - d - 1 with d = ref_logp - logp, loss = pg + beta*kl.
+ * [LIGER-BWD "Code analysis": the backward consumes logp, ref_logp, BETA and
+ *  the PPO-clipped flag; AXOLOTL part 1 (entropy), part 2 (selective
+ *  log-softmax)].  At GRPO_SEQUENCE, x is averaged over the valid tokens of
+ *  each sequence (mask-weighted, divided by max(count, 1)), ratio = e^{mean}
+ *  is written to seq_ratio[b] and pg is that sequence's, broadcast to all of
+ *  its tokens; the KL term stays per token.
+ *
+ * logits     [B*L, ld] of `dtype`            (in)
+ * ids        int64 [B*L] sampled token ids   (in)
+ * old_logp   fp32 [B*L]                      (in)
+ * ref_logp   fp32 [B*L] or NULL: NULL means no reference model (ref equals
+ *            the policy, kl = 0)             (in)
+ * adv        fp32 [B] advantage per sequence (in)
+ * mask       uint8 [B*L] completion mask or NULL (all ones); used only at
+ *            GRPO_SEQUENCE (per-token losses are reported for every token;
+ *            the caller's reduction applies the mask)  (in)
+ * loss, logp, lse  fp32 [B*L]                (out, required)
+ * entropy, kl      fp32 [B*L] or NULL        (out, optional)
+ * is_clipped uint8 [B*L] or NULL: 1 where the clipped branch is strictly the
+ *            smaller one (per sequence at GRPO_SEQUENCE)  (out, optional)
+ * gathered   fp32 [B*L] or NULL: z[r, ids[r]] upcast exactly  (out, optional)
+ * seq_ratio  fp32 [B]: required iff level == GRPO_SEQUENCE, else ignored (out)
+ * err_count  int32 [1] or NULL: += number of rows with an id outside [0, V)
+ * ------------------------------------------------------------------------ */
+int grpo_logits_fwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,
+                    int64_t ld, const int64_t* ids, const float* old_logp,
+                    const float* ref_logp, const float* adv, const uint8_t* mask,
+                    const grpo_params* p, float* loss, float* logp, float* lse,
+                    float* entropy, float* kl, uint8_t* is_clipped, float* gathered,
+                    float* seq_ratio, int32_t* err_count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * grpo_logits_bwd -- backward of sum_r dloss[r] * loss[r] w.r.t. the logits.
+ * Defines [LIGER-BWD "Code analysis", both kernels; "Why is this good"]:
+ *   token:    g = (-ratio*A*[not clipped] + beta*(1 - e^{ref - logp})) * dloss
+ *   sequence: g = -ratio_b*A_b*[not clipped_b] * (sum_t' dloss_bt') * m_bt/n_b
+ *                 + beta*(1 - e^{ref - logp}) * dloss_bt,  n_b = max(sum_t m, 1)
+ *   dlogits_j = g/T * (1[j == y] - e^{u_j - lse}).
+ * A row with g == 0 (zero advantage with no KL gradient, PPO-clipped token
+ * with beta == 0, or dloss == 0) is written as +0.0 without reading its
+ * logits.  ratio and the clipped flag are recomputed from logp and old_logp
+ * (token) or taken from seq_ratio (sequence) exactly as the forward did.
+ *
+ * logits, ids, old_logp, ref_logp, adv, mask, p: as for grpo_logits_fwd (in)
+ * logp, lse  fp32 [B*L] from grpo_logits_fwd (in, required)
+ * seq_ratio  fp32 [B] from grpo_logits_fwd; required iff GRPO_SEQUENCE (in)
+ * dloss      fp32 [B*L] upstream gradient of each token's loss (in)
+ * dlogits    [B*L, ld_out] of `dtype` (out); may alias logits if ld_out == ld
+ * zero_row   uint8 [B*L] or NULL: 1 where the row took the all-zero path
+ *            (that is, g == 0), even under GRPO_FLAG_FORCE_DENSE  (out)
+ * Rows with an id outside [0, V) are written as NaN.
+ * ------------------------------------------------------------------------ */
+int grpo_logits_bwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,
+                    int64_t ld, const int64_t* ids, const float* old_logp,
+                    const float* ref_logp, const float* adv, const uint8_t* mask,
+                    const grpo_params* p, const float* logp, const float* lse,
+                    const float* seq_ratio, const float* dloss, void* dlogits,
+                    int64_t ld_out, uint8_t* zero_row, void* stream);
+
+/* ------------------------------------------------------------------------
+ * entropy_from_logits -- per-row entropy of softmax(z / temperature).
+ * Defines [AXOLOTL part 1: minus the row sum of exp(logp) * logp of the row
+ * log-softmax; strided rows read in place].  temperature 1 is the plain op.
+ * logits [rows, ld] (in); entropy fp32 [rows] (out).  A row containing -inf
+ * has entropy NaN, as the definition's 0 * (-inf) gives.
+ * ------------------------------------------------------------------------ */
+int entropy_from_logits(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                        float temperature, float* entropy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * selective_log_softmax -- logp[r] = log_softmax(z_r / T)[ids[r]].
+ * Defines [AXOLOTL part 2].  logits [rows, ld], ids int64 [rows] (in);
+ * logp fp32 [rows] (out); lse fp32 [rows] or NULL (out; needed by the
+ * backward).  An id outside [0, V) gives NaN.
+ * ------------------------------------------------------------------------ */
+int selective_log_softmax(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                          const int64_t* ids, float temperature, float* logp, float* lse,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * selective_log_softmax_bwd -- custom backward of selective_log_softmax:
+ *   dlogits_j = grad_logp[r] / T * (1[j == ids[r]] - e^{z_j/T - lse[r]}).
+ * Defines [AXOLOTL part 2: the custom autograd backward].  Rows with
+ * grad_logp == 0 take the all-zero, write-only path.
+ * logits [rows, ld], ids, lse (from the forward), grad_logp fp32 [rows] (in);
+ * dlogits [rows, ld_out] of `dtype` (out; may alias logits if ld_out == ld).
+ * ------------------------------------------------------------------------ */
+int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64_t V,
+                              int64_t ld, const int64_t* ids, float temperature,
+                              const float* lse, const float* grad_logp, void* dlogits,
+                              int64_t ld_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fused_linear_grpo_chunk -- one batch chunk of the chunked fused-linear
+ * GRPO loss, gradients taken during the forward [LIGER-TRL items 3-4].
+ * For the chunk's R = nseq*L rows:
+ *   z = hidden * weight^T (fp32, in the workspace; never the whole batch),
+ *   token-level GRPO forward + backward of sum dloss*loss on z (fp32 rows),
+ *   *loss_accum += sum_r dloss[r] * loss[r],
+ *   grad_hidden = dz * weight            (overwritten, fp32 [R, H]),
+ *   grad_weight += dz^T * hidden         (accumulated, fp32 [V, H]),
+ * with dz rounded to bf16 before the two products.  The caller loops over
+ * chunks; level must be GRPO_TOKEN.
+ *
+ * hidden bf16 [R, H] row-major; weight bf16 [V, H] row-major (in)
+ * ids, old_logp, ref_logp (nullable), mask (nullable), dloss: [R] (in)
+ * adv fp32 [nseq] (in)
+ * loss_accum fp32 [1] (in/out, device); grad_hidden fp32 [R, H] (out);
+ * grad_weight fp32 [V, H] (in/out)
+ * workspace: device buffer of at least
+ *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned.
+ * H must be a multiple of 64 and at most 65536.
+ * ------------------------------------------------------------------------ */
+int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t H,
+                            const void* weight, int64_t V, const int64_t* ids,
+                            const float* old_logp, const float* ref_logp, const float* adv,
+                            const uint8_t* mask, const float* dloss, const grpo_params* p,
+                            float* loss_accum, float* grad_hidden, float* grad_weight,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fused_linear_grpo_chunk needs for R rows (0 on bad sizes). */
+size_t fused_linear_grpo_workspace_bytes(int64_t rows, int64_t V, int64_t H);
+
+/* Static, NUL-terminated description of a status code. */
+const char* grpo_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_ROWS_H */

@@ -1,0 +1,12 @@
+"""Row-wise GRPO logits pass for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The functions below are thin ctypes bindings of ``libgrpo_rows.so`` (built by
+``python -m rl_fine_tuning_row_amd.build``); PyTorch supplies device memory
+and the HIP stream only.
+"""
+from ._lib import (  # noqa: F401
+    GRPO_BF16, GRPO_F32, GRPO_FLAG_FORCE_DENSE, GRPO_SEQUENCE, GRPO_TOKEN, GrpoError,
+    GrpoParams, LIB_PATH, entropy_from_logits, fused_linear_grpo_chunk,
+    fused_linear_grpo_workspace_bytes, grpo_logits_bwd, grpo_logits_fwd, header_functions,
+    lib, selective_log_softmax, selective_log_softmax_bwd,
+)

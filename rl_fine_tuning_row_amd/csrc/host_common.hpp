@@ -1,0 +1,70 @@
+// host_common.hpp -- host-side argument checks shared by the entry points.
+// Plain C++: no device calls, so every check runs before anything is enqueued.
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "grpo_rows.h"
+
+namespace grpo {
+
+constexpr int64_t kMaxV = int64_t(1) << 26;        // row length limit (int32 lane indexing)
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // one workgroup per row
+
+inline int elem_size(int dtype) { return dtype == GRPO_BF16 ? 2 : 4; }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int check_dtype(int dtype) {
+  return (dtype == GRPO_F32 || dtype == GRPO_BF16) ? GRPO_OK : GRPO_ERR_DTYPE;
+}
+
+// logits-like matrix [rows, ld] with V used columns
+inline int check_matrix(const void* ptr, int dtype, int64_t rows, int64_t V, int64_t ld) {
+  int st = check_dtype(dtype);
+  if (st != GRPO_OK) return st;
+  if (rows < 0 || rows > kMaxRows || V <= 0 || V > kMaxV) return GRPO_ERR_SHAPE;
+  if (ld < V) return GRPO_ERR_STRIDE;
+  if (rows > 0 && ptr == nullptr) return GRPO_ERR_NULL;
+  if (!aligned(ptr, elem_size(dtype))) return GRPO_ERR_ALIGN;
+  return GRPO_OK;
+}
+
+inline int check_temperature(float T) {
+  return (std::isfinite(T) && T > 0.0f) ? GRPO_OK : GRPO_ERR_PARAM;
+}
+
+inline int check_params(const grpo_params* p) {
+  if (p == nullptr) return GRPO_ERR_NULL;
+  if (check_temperature(p->temperature) != GRPO_OK) return GRPO_ERR_PARAM;
+  if (!std::isfinite(p->beta) || p->beta < 0.0f) return GRPO_ERR_PARAM;
+  if (!std::isfinite(p->eps_low) || p->eps_low < 0.0f || p->eps_low >= 1.0f) return GRPO_ERR_PARAM;
+  if (!std::isfinite(p->eps_high) || p->eps_high < 0.0f) return GRPO_ERR_PARAM;
+  if (p->level != GRPO_TOKEN && p->level != GRPO_SEQUENCE) return GRPO_ERR_PARAM;
+  if ((p->flags & ~uint32_t(GRPO_FLAG_FORCE_DENSE)) != 0) return GRPO_ERR_PARAM;
+  return GRPO_OK;
+}
+
+inline int check_aligned4(const void* p) { return aligned(p, 4) ? GRPO_OK : GRPO_ERR_ALIGN; }
+
+// optional launch shape override "WG,UNROLL" for tuning sweeps; 0,0 = default
+struct LaunchOverride {
+  int wg = 0, unroll = 0;
+};
+inline LaunchOverride launch_override() {
+  static LaunchOverride o = [] {
+    LaunchOverride r;
+    const char* e = std::getenv("GRPO_ROWS_LAUNCH");
+    if (e != nullptr) {
+      char* end = nullptr;
+      r.wg = int(std::strtol(e, &end, 10));
+      if (end != nullptr && *end == ',') r.unroll = int(std::strtol(end + 1, nullptr, 10));
+    }
+    return r;
+  }();
+  return o;
+}
+
+}  // namespace grpo

@@ -1,0 +1,223 @@
+// row_core.hpp -- device building blocks of the row kernels (gfx950, wave64).
+//
+// One workgroup owns one row of V logits.  Each lane streams 128-bit vectors
+// (8 bf16 or 4 fp32) of the row, keeps a running softmax state in registers
+// and the workgroup merges the per-lane states once at the end:
+//
+//   m = running max of the raw logits z
+//   s = sum_j 2^{(z_j - m) c}                 c = log2(e) / T
+//   t = sum_j 2^{(z_j - m) c} (z_j - m) c     (only when the entropy is needed)
+//
+// so that, with u = z / T and M = m / T,
+//   lse = M + ln s,  logp_y = (z_y - m) / T - ln s,  H = ln s - ln(2) t / s.
+// This is the single-read online normaliser (Milakov & Gimelshein, "Online
+// normalizer calculation for softmax", 2018) extended with the entropy sum;
+// the max is refreshed once per register tile, not per element.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace grpo {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// initial running max: finite, so that empty lanes merge without inf - inf
+constexpr float kNegBig = -1e30f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.0f) & 0xffffu);
+}
+
+// element loads of either input dtype (uint16_t = bf16 bits)
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const uint16_t* p) {
+  return __uint_as_float(((uint32_t)*p) << 16);
+}
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = to_bf16(v); }
+
+// 128-bit vector of the input dtype
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* x) {
+    uint4 v;
+    v.x = pack_bf16x2(x[0], x[1]);
+    v.y = pack_bf16x2(x[2], x[3]);
+    v.z = pack_bf16x2(x[4], x[5]);
+    v.w = pack_bf16x2(x[6], x[7]);
+    return v;
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static uint4 pack(const float* x) {
+    uint4 v;
+    v.x = __float_as_uint(x[0]); v.y = __float_as_uint(x[1]);
+    v.z = __float_as_uint(x[2]); v.w = __float_as_uint(x[3]);
+    return v;
+  }
+};
+
+struct Stat {
+  float m, s, t;
+};
+
+__device__ __forceinline__ void stat_init(Stat& st) {
+  st.m = kNegBig;
+  st.s = 0.0f;
+  st.t = 0.0f;
+}
+
+// fold a register tile of K logits into the running state
+template <int K, bool NEED_T>
+__device__ __forceinline__ void stat_tile(Stat& st, const float* x, float c) {
+  float tm = x[0];
+#pragma unroll
+  for (int k = 1; k < K; ++k) tm = fmaxf(tm, x[k]);
+  const float mn = fmaxf(st.m, tm);
+  const float dl = (st.m - mn) * c;  // <= 0: rescale of the old sums
+  const float f = exp2_fast(dl);
+  if (NEED_T) st.t = f * fmaf(dl, st.s, st.t);
+  st.s = f * st.s;
+  st.m = mn;
+  const float mc = mn * c;
+  float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; k += 2) {
+    const float d0 = fmaf(x[k], c, -mc);
+    const float e0 = exp2_fast(d0);
+    s0 += e0;
+    if (NEED_T) t0 = fmaf(e0, d0, t0);
+    if (k + 1 < K) {
+      const float d1 = fmaf(x[k + 1], c, -mc);
+      const float e1 = exp2_fast(d1);
+      s1 += e1;
+      if (NEED_T) t1 = fmaf(e1, d1, t1);
+    }
+  }
+  st.s += s0 + s1;
+  if (NEED_T) st.t += t0 + t1;
+}
+
+template <bool NEED_T>
+__device__ __forceinline__ Stat stat_merge(const Stat& a, const Stat& b, float c) {
+  const float mn = fmaxf(a.m, b.m);
+  const float da = (a.m - mn) * c, db = (b.m - mn) * c;
+  const float fa = exp2_fast(da), fb = exp2_fast(db);
+  Stat r;
+  r.m = mn;
+  r.s = fa * a.s + fb * b.s;
+  r.t = NEED_T ? fa * fmaf(da, a.s, a.t) + fb * fmaf(db, b.s, b.t) : 0.0f;
+  return r;
+}
+
+template <bool NEED_T>
+__device__ __forceinline__ Stat wave_reduce_stat(Stat st, float c) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    Stat o;
+    o.m = __shfl_xor(st.m, off, 64);
+    o.s = __shfl_xor(st.s, off, 64);
+    o.t = NEED_T ? __shfl_xor(st.t, off, 64) : 0.0f;
+    st = stat_merge<NEED_T>(st, o, c);
+  }
+  return st;
+}
+
+// merge the per-lane states of the workgroup; the result is valid in every
+// lane.  Fixed merge order, so the result is deterministic.
+template <int WG, bool NEED_T>
+__device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
+  st = wave_reduce_stat<NEED_T>(st, c);
+  if constexpr (WG == 64) {
+    return st;
+  } else {
+    __shared__ Stat sh[WG / 64];
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = st;
+    __syncthreads();
+    Stat r = sh[0];
+#pragma unroll
+    for (int k = 1; k < WG / 64; ++k) r = stat_merge<NEED_T>(r, sh[k], c);
+    return r;
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// deterministic workgroup sum of two floats; valid in every lane.
+// `sh` must hold 2 * WG / 64 floats; callers pass distinct buffers for
+// back-to-back calls.
+template <int WG>
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* sh) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if constexpr (WG > 64) {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      sh[w] = a;
+      sh[WG / 64 + w] = b;
+    }
+    __syncthreads();
+    a = sh[0];
+    b = sh[WG / 64];
+#pragma unroll
+    for (int k = 1; k < WG / 64; ++k) {
+      a += sh[k];
+      b += sh[WG / 64 + k];
+    }
+  }
+}
+
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// PPO clipped-ratio terms with NaN propagation (plain comparisons, not
+// fminf/fmaxf, which would drop a NaN ratio).
+struct Ppo {
+  float ratio, pg;
+  bool clipped;
+};
+__device__ __forceinline__ Ppo ppo_terms(float logratio, float A, float lo, float hi) {
+  Ppo r;
+  r.ratio = expf(logratio);
+  const float cr = r.ratio < lo ? lo : (r.ratio > hi ? hi : r.ratio);
+  const float pa = r.ratio * A, ca = cr * A;
+  r.clipped = ca < pa;
+  r.pg = -(r.clipped ? ca : pa);
+  return r;
+}
+
+}  // namespace grpo

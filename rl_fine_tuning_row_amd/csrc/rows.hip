@@ -1,0 +1,645 @@
+// rows.hip -- HBM-bound row kernels and their C ABI entry points:
+// grpo_logits_fwd, grpo_logits_bwd, entropy_from_logits,
+// selective_log_softmax, selective_log_softmax_bwd.
+//
+// One workgroup per row.  Lanes stream the row with 128-bit loads (8 bf16 or
+// 4 fp32 per lane), UNROLL vectors in flight per lane, fold each register
+// tile into the online softmax state (row_core.hpp), reduce across the wave
+// with lane shuffles and across waves through LDS, and lane 0 writes the
+// per-row scalars.  The backward computes the row's dlogp first; it is the
+// same in every lane (readfirstlane), so the all-zero early path
+// [Liger-Kernel PR #1550 analysis, "Code analysis": the added
+// ``if dlogp == 0.0`` early return] is a scalar branch that writes zeros
+// without touching the logits.
+#include <hip/hip_runtime.h>
+
+#include "grpo_rows.h"
+#include "host_common.hpp"
+#include "row_core.hpp"
+
+namespace grpo {
+
+enum FwdMode : int32_t { FWD_GRPO = 0, FWD_ENTROPY = 1, FWD_LSM = 2 };
+enum BwdMode : int32_t { BWD_GRPO = 0, BWD_LSM = 1 };
+
+struct FwdArgs {
+  const void* logits;
+  int64_t ld;
+  int32_t V;
+  int32_t L;  // tokens per sequence (GRPO); 1 otherwise
+  const int64_t* ids;
+  const float* old_logp;
+  const float* ref_logp;
+  const float* adv;
+  float T, c, beta, lo, hi;
+  int32_t mode, level;
+  float* loss;
+  float* logp;
+  float* lse;
+  float* entropy;
+  float* kl;
+  uint8_t* is_clipped;
+  float* gathered;
+  int32_t* err_count;
+};
+
+struct BwdArgs {
+  const void* logits;
+  int64_t ld;
+  void* dlogits;
+  int64_t ld_out;
+  int32_t V;
+  int32_t L;
+  const int64_t* ids;
+  const float* old_logp;
+  const float* ref_logp;
+  const float* adv;
+  const uint8_t* mask;
+  const float* logp;
+  const float* lse;
+  const float* seq_ratio;
+  const float* dloss;  // grad_logp in BWD_LSM mode
+  float T, c, beta, lo, hi;
+  int32_t mode, level, force_dense;
+  uint8_t* zero_row;
+};
+
+struct SeqArgs {
+  int32_t L;
+  const float* logp;
+  const float* old_logp;
+  const uint8_t* mask;
+  const float* adv;
+  float lo, hi;
+  float* loss;
+  uint8_t* is_clipped;
+  float* seq_ratio;
+};
+
+// ---------------------------------------------------------------------------
+// forward: one pass over the row
+// ---------------------------------------------------------------------------
+template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T>
+__device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, float c) {
+  Stat st;
+  stat_init(st);
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    constexpr int VE = Vec<TIn>::N;
+    const uint4* __restrict__ rv = reinterpret_cast<const uint4*>(row);
+    const int nvec = V / VE;
+    int i = tid;
+    for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
+      uint4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) v[u] = rv[i + u * WG];
+      float x[UNROLL * VE];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) Vec<TIn>::unpack(v[u], x + u * VE);
+      stat_tile<UNROLL * VE, NEED_T>(st, x, c);
+    }
+    for (; i < nvec; i += WG) {
+      float x[VE];
+      Vec<TIn>::unpack(rv[i], x);
+      stat_tile<VE, NEED_T>(st, x, c);
+    }
+    const int j = nvec * VE + tid;
+    if (j < V) {
+      const float x = load_elem(row + j);
+      stat_tile<1, NEED_T>(st, &x, c);
+    }
+  } else {
+    constexpr int K = 4 * UNROLL;
+    int j = tid;
+    for (; j + (K - 1) * WG < V; j += K * WG) {
+      float x[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) x[k] = load_elem(row + j + k * WG);
+      stat_tile<K, NEED_T>(st, x, c);
+    }
+    for (; j < V; j += WG) {
+      const float x = load_elem(row + j);
+      stat_tile<1, NEED_T>(st, &x, c);
+    }
+  }
+  return st;
+}
+
+template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T>
+__global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
+  const int64_t r = blockIdx.x;
+  const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
+  const Stat st = block_reduce_stat<WG, NEED_T>(
+      scan_row<TIn, WG, UNROLL, VEC, NEED_T>(row, a.V, a.c), a.c);
+  if (threadIdx.x != 0) return;
+
+  const float logS = logf(st.s);
+  const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
+  if (a.mode == FWD_ENTROPY) {
+    a.entropy[r] = H;
+    return;
+  }
+  const int64_t y = a.ids[r];
+  const bool valid = y >= 0 && y < a.V;
+  const float zy = valid ? load_elem(row + y) : __builtin_nanf("");
+  if (!valid && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+  const float lse = st.m / a.T + logS;
+  const float logp = (zy - st.m) / a.T - logS;
+  if (a.mode == FWD_LSM) {
+    a.logp[r] = logp;
+    if (a.lse != nullptr) a.lse[r] = lse;
+    return;
+  }
+  // GRPO per-token epilogue
+  a.logp[r] = logp;
+  a.lse[r] = lse;
+  if (a.entropy != nullptr) a.entropy[r] = H;
+  if (a.gathered != nullptr) a.gathered[r] = zy;
+  float kl = 0.0f;
+  if (a.ref_logp != nullptr) {
+    const float d = a.ref_logp[r] - logp;
+    kl = expm1f(d) - d;
+  }
+  if (a.kl != nullptr) a.kl[r] = kl;
+  const float kl_term = a.beta != 0.0f ? a.beta * kl : 0.0f;
+  if (a.level == GRPO_TOKEN) {
+    const Ppo q = ppo_terms(logp - a.old_logp[r], a.adv[r / a.L], a.lo, a.hi);
+    a.loss[r] = q.pg + kl_term;
+    if (a.is_clipped != nullptr) a.is_clipped[r] = q.clipped ? 1 : 0;
+  } else {
+    a.loss[r] = kl_term;  // the sequence epilogue adds the sequence's pg
+  }
+}
+
+// sequence level: one workgroup per sequence; mask-weighted mean log-ratio,
+// one clipped ratio per sequence, pg broadcast to the sequence's tokens.
+__global__ __launch_bounds__(256) void seq_fwd_epilogue_kernel(SeqArgs a) {
+  const int64_t b = blockIdx.x;
+  const int64_t base = b * a.L;
+  float sx = 0.0f, sm = 0.0f;
+  for (int t = threadIdx.x; t < a.L; t += 256) {
+    const float m = a.mask != nullptr ? float(a.mask[base + t]) : 1.0f;
+    sx += m * (a.logp[base + t] - a.old_logp[base + t]);
+    sm += m;
+  }
+  __shared__ float sh[8];
+  block_sum2<256>(sx, sm, sh);
+  const float n = fmaxf(sm, 1.0f);
+  const Ppo q = ppo_terms(sx / n, a.adv[b], a.lo, a.hi);
+  if (threadIdx.x == 0) a.seq_ratio[b] = q.ratio;
+  for (int t = threadIdx.x; t < a.L; t += 256) {
+    a.loss[base + t] += q.pg;
+    if (a.is_clipped != nullptr) a.is_clipped[base + t] = q.clipped ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+template <typename TIn, int WG>
+__device__ __forceinline__ float row_dlogp(const BwdArgs& a, int64_t r) {
+  if (a.mode == BWD_LSM) return a.dloss[r];
+  const float logp = a.logp[r];
+  const float w = a.dloss[r];
+  float klg = 0.0f;
+  if (a.ref_logp != nullptr && a.beta != 0.0f) klg = -a.beta * expm1f(a.ref_logp[r] - logp);
+  if (a.level == GRPO_TOKEN) {
+    const float A = a.adv[r / a.L];
+    const Ppo q = ppo_terms(logp - a.old_logp[r], A, a.lo, a.hi);
+    const float pgg = q.clipped ? 0.0f : -q.ratio * A;
+    return (pgg + klg) * w;
+  }
+  // sequence level: per-sequence sums of dloss and of the mask
+  const int64_t b = r / a.L;
+  const int64_t base = b * a.L;
+  float ws = 0.0f, ms = 0.0f;
+  for (int t = threadIdx.x; t < a.L; t += WG) {
+    ws += a.dloss[base + t];
+    ms += a.mask != nullptr ? float(a.mask[base + t]) : 1.0f;
+  }
+  __shared__ float sh[2 * (WG / 64)];
+  block_sum2<WG>(ws, ms, sh);
+  const float n = fmaxf(ms, 1.0f);
+  const float ratio = a.seq_ratio[b];
+  const float A = a.adv[b];
+  const float cr = ratio < a.lo ? a.lo : (ratio > a.hi ? a.hi : ratio);
+  const bool clipped = cr * A < ratio * A;
+  const float coef = clipped ? 0.0f : -ratio * A;
+  const float m = a.mask != nullptr ? float(a.mask[r]) : 1.0f;
+  return coef * ws * m / n + klg * w;
+}
+
+template <typename TIn, int WG, bool VEC>
+__device__ __forceinline__ void fill_row(TIn* __restrict__ out, int V, float value) {
+  if constexpr (VEC) {
+    constexpr int VE = Vec<TIn>::N;
+    float x[VE];
+#pragma unroll
+    for (int k = 0; k < VE; ++k) x[k] = value;
+    const uint4 pv = Vec<TIn>::pack(x);
+    uint4* __restrict__ ov = reinterpret_cast<uint4*>(out);
+    const int nvec = V / VE;
+    for (int i = threadIdx.x; i < nvec; i += WG) ov[i] = pv;
+    const int j = nvec * VE + threadIdx.x;
+    if (j < V) store_elem(out + j, value);
+  } else {
+    for (int j = threadIdx.x; j < V; j += WG) store_elem(out + j, value);
+  }
+}
+
+template <typename TIn, int WG, int UNROLL, bool VEC>
+__global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
+  const int64_t r = blockIdx.x;
+  const float g = uniform(row_dlogp<TIn, WG>(a, r));
+  const int64_t y = a.ids[r];
+  const bool valid = y >= 0 && y < a.V;
+  TIn* __restrict__ out = static_cast<TIn*>(a.dlogits) + r * a.ld_out;
+  const bool zero = (g == 0.0f);
+  if (threadIdx.x == 0 && a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
+  if (!valid) {
+    fill_row<TIn, WG, false>(out, a.V, __builtin_nanf(""));
+    return;
+  }
+  if (zero && !a.force_dense) {  // early path: no logits read, no exp
+    fill_row<TIn, WG, VEC>(out, a.V, 0.0f);
+    return;
+  }
+  const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
+  const float coef = g / a.T;
+  const float lse2 = a.lse[r] * kLog2e;
+  const float c = a.c;
+  const int yi = int(y);
+  if constexpr (VEC) {
+    constexpr int VE = Vec<TIn>::N;
+    const uint4* rv = reinterpret_cast<const uint4*>(row);
+    uint4* ov = reinterpret_cast<uint4*>(out);
+    const int nvec = a.V / VE;
+    const int vy = yi / VE, ky = yi % VE;
+    int i = threadIdx.x;
+    for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
+      uint4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) v[u] = rv[i + u * WG];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float x[VE];
+        Vec<TIn>::unpack(v[u], x);
+#pragma unroll
+        for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
+        if (i + u * WG == vy) {
+#pragma unroll
+          for (int k = 0; k < VE; ++k)
+            if (k == ky) x[k] += coef;
+        }
+        ov[i + u * WG] = Vec<TIn>::pack(x);
+      }
+    }
+    for (; i < nvec; i += WG) {
+      float x[VE];
+      Vec<TIn>::unpack(rv[i], x);
+#pragma unroll
+      for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
+      if (i == vy) {
+#pragma unroll
+        for (int k = 0; k < VE; ++k)
+          if (k == ky) x[k] += coef;
+      }
+      ov[i] = Vec<TIn>::pack(x);
+    }
+    const int j = nvec * VE + threadIdx.x;
+    if (j < a.V) {
+      float d = -coef * exp2_fast(fmaf(load_elem(row + j), c, -lse2));
+      if (j == yi) d += coef;
+      store_elem(out + j, d);
+    }
+  } else {
+    for (int j = threadIdx.x; j < a.V; j += WG) {
+      float d = -coef * exp2_fast(fmaf(load_elem(row + j), c, -lse2));
+      if (j == yi) d += coef;
+      store_elem(out + j, d);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch shape dispatch
+// ---------------------------------------------------------------------------
+struct Shape {
+  int wg, unroll;
+};
+
+// default shapes: one workgroup per row; wider workgroups for longer rows
+inline Shape pick_shape(int64_t V, int es) {
+  const LaunchOverride o = launch_override();
+  if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
+  const int64_t bytes = V * es;
+  if (bytes <= 16 * 1024) return {256, 2};
+  if (bytes <= 128 * 1024) return {256, 4};
+  return {512, 4};
+}
+
+#define GRPO_SHAPES(X) \
+  X(64, 4)             \
+  X(128, 4)            \
+  X(256, 2)            \
+  X(256, 4)            \
+  X(256, 8)            \
+  X(512, 2)            \
+  X(512, 4)            \
+  X(1024, 2)           \
+  X(1024, 4)
+
+template <typename TIn, bool VEC, bool NEED_T>
+hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
+  if constexpr (!VEC) {
+    hipLaunchKernelGGL((row_fwd_kernel<TIn, 256, 4, false, NEED_T>), dim3(unsigned(rows)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+  } else {
+#define X(W, U)                                                                          \
+  if (sh.wg == W && sh.unroll == U) {                                                     \
+    hipLaunchKernelGGL((row_fwd_kernel<TIn, W, U, true, NEED_T>), dim3(unsigned(rows)),   \
+                       dim3(W), 0, s, a);                                                 \
+    return hipGetLastError();                                                             \
+  }
+    GRPO_SHAPES(X)
+#undef X
+    return hipErrorInvalidConfiguration;
+  }
+}
+
+template <typename TIn, bool VEC>
+hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
+  if constexpr (!VEC) {
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, 256, 4, false>), dim3(unsigned(rows)), dim3(256),
+                       0, s, a);
+    return hipGetLastError();
+  } else {
+#define X(W, U)                                                                           \
+  if (sh.wg == W && sh.unroll == U) {                                                      \
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, W, U, true>), dim3(unsigned(rows)), dim3(W), 0, \
+                       s, a);                                                              \
+    return hipGetLastError();                                                              \
+  }
+    GRPO_SHAPES(X)
+#undef X
+    return hipErrorInvalidConfiguration;
+  }
+}
+#undef GRPO_SHAPES
+
+inline bool rows_vec_ok(const void* p, int64_t ld, int es) {
+  return aligned(p, 16) && ((ld * es) % 16) == 0;
+}
+
+int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s) {
+  const int es = elem_size(dtype);
+  const Shape sh = pick_shape(a.V, es);
+  const bool vec = rows_vec_ok(a.logits, a.ld, es);
+  hipError_t e;
+  if (dtype == GRPO_BF16) {
+    if (vec) e = need_t ? launch_fwd_t<uint16_t, true, true>(a, rows, sh, s)
+                        : launch_fwd_t<uint16_t, true, false>(a, rows, sh, s);
+    else e = need_t ? launch_fwd_t<uint16_t, false, true>(a, rows, sh, s)
+                    : launch_fwd_t<uint16_t, false, false>(a, rows, sh, s);
+  } else {
+    if (vec) e = need_t ? launch_fwd_t<float, true, true>(a, rows, sh, s)
+                        : launch_fwd_t<float, true, false>(a, rows, sh, s);
+    else e = need_t ? launch_fwd_t<float, false, true>(a, rows, sh, s)
+                    : launch_fwd_t<float, false, false>(a, rows, sh, s);
+  }
+  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
+  const int es = elem_size(dtype);
+  const Shape sh = pick_shape(a.V, es);
+  const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
+  hipError_t e;
+  if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, true>(a, rows, sh, s)
+                                  : launch_bwd_t<uint16_t, false>(a, rows, sh, s);
+  else e = vec ? launch_bwd_t<float, true>(a, rows, sh, s) : launch_bwd_t<float, false>(a, rows, sh, s);
+  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+}  // namespace grpo
+
+using namespace grpo;
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_grpo_common(const void* logits, int dtype, int64_t B, int64_t L, int64_t V, int64_t ld,
+                      const int64_t* ids, const float* old_logp, const float* ref_logp,
+                      const float* adv, const uint8_t* mask, const grpo_params* p) {
+  if (B < 0 || L < 0 || (B > 0 && L == 0) || L > kMaxRows || (L > 0 && B > kMaxRows / L))
+    return GRPO_ERR_SHAPE;
+  int st = check_matrix(logits, dtype, B * L, V, ld);
+  if (st != GRPO_OK) return st;
+  st = check_params(p);
+  if (st != GRPO_OK) return st;
+  if (B * L > 0 && (ids == nullptr || old_logp == nullptr || adv == nullptr)) return GRPO_ERR_NULL;
+  if (!aligned(ids, 8) || !aligned(old_logp, 4) || !aligned(ref_logp, 4) || !aligned(adv, 4))
+    return GRPO_ERR_ALIGN;
+  (void)mask;
+  return GRPO_OK;
+}
+
+void fill_loss_params(const grpo_params* p, float& T, float& c, float& lo, float& hi) {
+  T = p->temperature;
+  c = kLog2e / T;
+  lo = 1.0f - p->eps_low;
+  hi = 1.0f + p->eps_high;
+}
+
+}  // namespace
+
+extern "C" int grpo_logits_fwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,
+                               int64_t ld, const int64_t* ids, const float* old_logp,
+                               const float* ref_logp, const float* adv, const uint8_t* mask,
+                               const grpo_params* p, float* loss, float* logp, float* lse,
+                               float* entropy, float* kl, uint8_t* is_clipped, float* gathered,
+                               float* seq_ratio, int32_t* err_count, void* stream) {
+  int st = check_grpo_common(logits, dtype, B, L, V, ld, ids, old_logp, ref_logp, adv, mask, p);
+  if (st != GRPO_OK) return st;
+  const int64_t rows = B * L;
+  if (rows > 0 && (loss == nullptr || logp == nullptr || lse == nullptr)) return GRPO_ERR_NULL;
+  if (rows > 0 && p->level == GRPO_SEQUENCE && seq_ratio == nullptr) return GRPO_ERR_NULL;
+  for (const void* q : {(const void*)loss, (const void*)logp, (const void*)lse,
+                        (const void*)entropy, (const void*)kl, (const void*)gathered,
+                        (const void*)seq_ratio, (const void*)err_count})
+    if (!aligned(q, 4)) return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  FwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.V = int32_t(V);
+  a.L = int32_t(L);
+  a.ids = ids;
+  a.old_logp = old_logp;
+  a.ref_logp = ref_logp;
+  a.adv = adv;
+  fill_loss_params(p, a.T, a.c, a.lo, a.hi);
+  a.beta = p->beta;
+  a.mode = FWD_GRPO;
+  a.level = p->level;
+  a.loss = loss;
+  a.logp = logp;
+  a.lse = lse;
+  a.entropy = entropy;
+  a.kl = kl;
+  a.is_clipped = is_clipped;
+  a.gathered = gathered;
+  a.err_count = err_count;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_fwd(a, dtype, rows, entropy != nullptr, s);
+  if (st != GRPO_OK || p->level != GRPO_SEQUENCE) return st;
+  SeqArgs q{};
+  q.L = int32_t(L);
+  q.logp = logp;
+  q.old_logp = old_logp;
+  q.mask = mask;
+  q.adv = adv;
+  q.lo = a.lo;
+  q.hi = a.hi;
+  q.loss = loss;
+  q.is_clipped = is_clipped;
+  q.seq_ratio = seq_ratio;
+  hipLaunchKernelGGL(seq_fwd_epilogue_kernel, dim3(unsigned(B)), dim3(256), 0, s, q);
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+extern "C" int grpo_logits_bwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,
+                               int64_t ld, const int64_t* ids, const float* old_logp,
+                               const float* ref_logp, const float* adv, const uint8_t* mask,
+                               const grpo_params* p, const float* logp, const float* lse,
+                               const float* seq_ratio, const float* dloss, void* dlogits,
+                               int64_t ld_out, uint8_t* zero_row, void* stream) {
+  int st = check_grpo_common(logits, dtype, B, L, V, ld, ids, old_logp, ref_logp, adv, mask, p);
+  if (st != GRPO_OK) return st;
+  const int64_t rows = B * L;
+  if (ld_out < V) return GRPO_ERR_STRIDE;
+  if (dlogits == logits && ld_out != ld) return GRPO_ERR_STRIDE;
+  if (rows > 0 && (logp == nullptr || lse == nullptr || dloss == nullptr || dlogits == nullptr))
+    return GRPO_ERR_NULL;
+  if (rows > 0 && p->level == GRPO_SEQUENCE && seq_ratio == nullptr) return GRPO_ERR_NULL;
+  if (!aligned(logp, 4) || !aligned(lse, 4) || !aligned(dloss, 4) || !aligned(seq_ratio, 4) ||
+      !aligned(dlogits, elem_size(dtype)))
+    return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  BwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.dlogits = dlogits;
+  a.ld_out = ld_out;
+  a.V = int32_t(V);
+  a.L = int32_t(L);
+  a.ids = ids;
+  a.old_logp = old_logp;
+  a.ref_logp = ref_logp;
+  a.adv = adv;
+  a.mask = mask;
+  a.logp = logp;
+  a.lse = lse;
+  a.seq_ratio = seq_ratio;
+  a.dloss = dloss;
+  fill_loss_params(p, a.T, a.c, a.lo, a.hi);
+  a.beta = p->beta;
+  a.mode = BWD_GRPO;
+  a.level = p->level;
+  a.force_dense = (p->flags & GRPO_FLAG_FORCE_DENSE) ? 1 : 0;
+  a.zero_row = zero_row;
+  return launch_bwd(a, dtype, rows, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int entropy_from_logits(const void* logits, int dtype, int64_t rows, int64_t V,
+                                   int64_t ld, float temperature, float* entropy,
+                                   void* stream) {
+  int st = check_matrix(logits, dtype, rows, V, ld);
+  if (st != GRPO_OK) return st;
+  if (check_temperature(temperature) != GRPO_OK) return GRPO_ERR_PARAM;
+  if (rows > 0 && entropy == nullptr) return GRPO_ERR_NULL;
+  if (!aligned(entropy, 4)) return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  FwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.V = int32_t(V);
+  a.L = 1;
+  a.T = temperature;
+  a.c = kLog2e / temperature;
+  a.mode = FWD_ENTROPY;
+  a.entropy = entropy;
+  return launch_fwd(a, dtype, rows, true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int selective_log_softmax(const void* logits, int dtype, int64_t rows, int64_t V,
+                                     int64_t ld, const int64_t* ids, float temperature,
+                                     float* logp, float* lse, void* stream) {
+  int st = check_matrix(logits, dtype, rows, V, ld);
+  if (st != GRPO_OK) return st;
+  if (check_temperature(temperature) != GRPO_OK) return GRPO_ERR_PARAM;
+  if (rows > 0 && (ids == nullptr || logp == nullptr)) return GRPO_ERR_NULL;
+  if (!aligned(ids, 8) || !aligned(logp, 4) || !aligned(lse, 4)) return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  FwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.V = int32_t(V);
+  a.L = 1;
+  a.ids = ids;
+  a.T = temperature;
+  a.c = kLog2e / temperature;
+  a.mode = FWD_LSM;
+  a.logp = logp;
+  a.lse = lse;
+  return launch_fwd(a, dtype, rows, false, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64_t V,
+                                         int64_t ld, const int64_t* ids, float temperature,
+                                         const float* lse, const float* grad_logp,
+                                         void* dlogits, int64_t ld_out, void* stream) {
+  int st = check_matrix(logits, dtype, rows, V, ld);
+  if (st != GRPO_OK) return st;
+  if (check_temperature(temperature) != GRPO_OK) return GRPO_ERR_PARAM;
+  if (ld_out < V) return GRPO_ERR_STRIDE;
+  if (dlogits == logits && ld_out != ld) return GRPO_ERR_STRIDE;
+  if (rows > 0 && (ids == nullptr || lse == nullptr || grad_logp == nullptr || dlogits == nullptr))
+    return GRPO_ERR_NULL;
+  if (!aligned(ids, 8) || !aligned(lse, 4) || !aligned(grad_logp, 4) ||
+      !aligned(dlogits, elem_size(dtype)))
+    return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  BwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.dlogits = dlogits;
+  a.ld_out = ld_out;
+  a.V = int32_t(V);
+  a.L = 1;
+  a.ids = ids;
+  a.lse = lse;
+  a.dloss = grad_logp;
+  a.T = temperature;
+  a.c = kLog2e / temperature;
+  a.mode = BWD_LSM;
+  return launch_bwd(a, dtype, rows, static_cast<hipStream_t>(stream));
+}
+
+extern "C" const char* grpo_status_string(int status) {
+  switch (status) {
+    case GRPO_OK: return "ok";
+    case GRPO_ERR_NULL: return "a required pointer is NULL";
+    case GRPO_ERR_SHAPE: return "a size is out of range";
+    case GRPO_ERR_STRIDE: return "row stride smaller than V, or in-place with a different stride";
+    case GRPO_ERR_DTYPE: return "unknown dtype";
+    case GRPO_ERR_ALIGN: return "pointer not aligned to its element size";
+    case GRPO_ERR_WORKSPACE: return "workspace NULL or too small";
+    case GRPO_ERR_LAUNCH: return "kernel launch failed";
+    case GRPO_ERR_PARAM: return "invalid loss parameter";
+    default: return "unknown status";
+  }
+}

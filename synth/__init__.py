@@ -334,3 +334,31 @@ def fused_case(seed: int = 0, B: int = 32, L: int = 1024, H: int = 1024, V: int 
 def add_noise_f32(logp_true: np.ndarray, noise: np.ndarray) -> np.ndarray:
     """old/ref log-probabilities: true policy logp plus noise, stored as fp32."""
     return (np.asarray(logp_true, np.float64) + np.asarray(noise, np.float64)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# stored policy log-probabilities (written by tests/golden/make_oracle_logp.py)
+# --------------------------------------------------------------------------
+_GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       "tests", "golden")
+
+
+def load_stored_logp(name: str, check_rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """float64 [B*L] policy logp of the named workload ("token", "sequence",
+    "fused").  ``check_rows``: the generator's bits for the stored check rows,
+    compared against the stored digest (raises if the inputs have drifted)."""
+    import hashlib
+    import json
+    with open(os.path.join(_GOLDEN, f"oracle_logp_{name}.json")) as f:
+        meta = json.load(f)
+    if check_rows is not None:
+        d = hashlib.sha256(np.ascontiguousarray(check_rows).tobytes()).hexdigest()
+        if not meta["check_digest"].startswith(d):
+            raise RuntimeError(f"stored logp '{name}' does not match the generated inputs")
+    return np.load(os.path.join(_GOLDEN, f"oracle_logp_{name}.npy"))
+
+
+def stored_check_rows(name: str):
+    import json
+    with open(os.path.join(_GOLDEN, f"oracle_logp_{name}.json")) as f:
+        return json.load(f)["check_rows"]
