@@ -144,14 +144,21 @@ def main():
     kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
               eps_high=case.eps_high, level="token")
 
+    # arguments are marshalled once per buffer set; a step is two C calls
+    for s in sets:
+        s["fwd"], _ = grl.grpo_logits_fwd(s["z"], ids, old_t, adv, B, L, mask=mask,
+                                          out=s["out"], prepare=True, **kw)
+        s["bwd"], _, _ = grl.grpo_logits_bwd(s["z"], ids, old_t, adv, B, L, s["out"]["logp"],
+                                             s["out"]["lse"], dloss, mask=mask, dlogits=s["dz"],
+                                             zero_row=s["zr"], prepare=True, **kw)
+
     def step(s, ev=None):
         if ev is not None:
             ev[0].record()
-        grl.grpo_logits_fwd(s["z"], ids, old_t, adv, B, L, mask=mask, out=s["out"], **kw)
+        s["fwd"]()
         if ev is not None:
             ev[1].record()
-        grl.grpo_logits_bwd(s["z"], ids, old_t, adv, B, L, s["out"]["logp"], s["out"]["lse"],
-                            dloss, mask=mask, dlogits=s["dz"], zero_row=s["zr"], **kw)
+        s["bwd"]()
         if ev is not None:
             ev[2].record()
 

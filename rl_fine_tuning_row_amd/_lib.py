@@ -138,13 +138,28 @@ def _check(fn, status):
         raise GrpoError(fn, status)
 
 
+def _launcher(name, cargs, keep=()):
+    """Zero-argument callable that enqueues ``name(*cargs)`` and raises on a
+    non-zero status.  ``keep`` holds objects the marshalled arguments point to."""
+    fn = getattr(lib(), name)
+
+    def launch(_keep=keep):
+        st = fn(*cargs)
+        if st != 0:
+            raise GrpoError(name, st)
+    return launch
+
+
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
 def grpo_logits_fwd(logits, ids, old_logp, adv, B, L, *, ref_logp=None, mask=None,
                     temperature=1.0, beta=0.0, eps_low=0.2, eps_high=0.2, level="token",
                     entropy=True, kl=True, is_clipped=True, gathered=False,
-                    err_count=None, out=None, stream=None) -> dict:
+                    err_count=None, out=None, stream=None, prepare=False):
+    """Returns the dict of outputs.  With ``prepare=True`` nothing is launched:
+    returns (launch, outputs) where ``launch()`` enqueues the call with the
+    arguments marshalled once (for tight timing loops)."""
     rows, V, ld = _rows_view(logits)
     if rows != B * L:
         raise ValueError(f"logits has {rows} rows, expected B*L = {B * L}")
@@ -172,19 +187,22 @@ def grpo_logits_fwd(logits, ids, old_logp, adv, B, L, *, ref_logp=None, mask=Non
             get("entropy", f32, rows, entropy), get("kl", f32, rows, kl),
             get("is_clipped", torch.uint8, rows, is_clipped),
             get("gathered", f32, rows, gathered), get("seq_ratio", f32, B, seq)]
-    st = lib().grpo_logits_fwd(_ptr(logits), _dtype_code(logits), B, L, V, ld, _ptr(ids),
-                               _ptr(old_logp), _ptr(ref_logp), _ptr(adv), _ptr(mask),
-                               ctypes.byref(p), *[_ptr(t) for t in args], _ptr(err_count),
-                               _stream(stream))
-    _check("grpo_logits_fwd", st)
+    cargs = (_ptr(logits), _dtype_code(logits), B, L, V, ld, _ptr(ids), _ptr(old_logp),
+             _ptr(ref_logp), _ptr(adv), _ptr(mask), ctypes.byref(p), *[_ptr(t) for t in args],
+             _ptr(err_count), _stream(stream))
+    launch = _launcher("grpo_logits_fwd", cargs, keep=(p,))
+    if prepare:
+        return launch, o
+    launch()
     return o
 
 
 def grpo_logits_bwd(logits, ids, old_logp, adv, B, L, logp, lse, dloss, *, ref_logp=None,
                     mask=None, seq_ratio=None, temperature=1.0, beta=0.0, eps_low=0.2,
                     eps_high=0.2, level="token", force_dense=False, dlogits=None,
-                    zero_row=True, stream=None):
-    """Returns (dlogits, zero_row or None)."""
+                    zero_row=True, stream=None, prepare=False):
+    """Returns (dlogits, zero_row or None); with ``prepare=True`` returns
+    (launch, dlogits, zero_row) without launching."""
     rows, V, ld = _rows_view(logits)
     if rows != B * L:
         raise ValueError(f"logits has {rows} rows, expected B*L = {B * L}")
@@ -207,11 +225,13 @@ def grpo_logits_bwd(logits, ids, old_logp, adv, B, L, logp, lse, dloss, *, ref_l
         zr = _need(zero_row, torch.uint8, rows, "zero_row")
     p = _params(temperature, beta, eps_low, eps_high, level,
                 GRPO_FLAG_FORCE_DENSE if force_dense else 0)
-    st = lib().grpo_logits_bwd(_ptr(logits), _dtype_code(logits), B, L, V, ld, _ptr(ids),
-                               _ptr(old_logp), _ptr(ref_logp), _ptr(adv), _ptr(mask),
-                               ctypes.byref(p), _ptr(logp), _ptr(lse), _ptr(seq_ratio),
-                               _ptr(dloss), _ptr(dlogits), ld_out, _ptr(zr), _stream(stream))
-    _check("grpo_logits_bwd", st)
+    cargs = (_ptr(logits), _dtype_code(logits), B, L, V, ld, _ptr(ids), _ptr(old_logp),
+             _ptr(ref_logp), _ptr(adv), _ptr(mask), ctypes.byref(p), _ptr(logp), _ptr(lse),
+             _ptr(seq_ratio), _ptr(dloss), _ptr(dlogits), ld_out, _ptr(zr), _stream(stream))
+    launch = _launcher("grpo_logits_bwd", cargs, keep=(p,))
+    if prepare:
+        return launch, dlogits, zr
+    launch()
     return dlogits, zr
 
 

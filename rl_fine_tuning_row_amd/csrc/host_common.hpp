@@ -49,22 +49,27 @@ inline int check_params(const grpo_params* p) {
 
 inline int check_aligned4(const void* p) { return aligned(p, 4) ? GRPO_OK : GRPO_ERR_ALIGN; }
 
-// optional launch shape override "WG,UNROLL" for tuning sweeps; 0,0 = default
+// optional launch shape overrides "WG,UNROLL" for tuning sweeps:
+// GRPO_ROWS_FWD_LAUNCH (forward-type kernels), GRPO_ROWS_BWD_LAUNCH
+// (backward-type kernels), GRPO_ROWS_LAUNCH (both).  Unset: built-in policy.
 struct LaunchOverride {
   int wg = 0, unroll = 0;
 };
-inline LaunchOverride launch_override() {
-  static LaunchOverride o = [] {
-    LaunchOverride r;
-    const char* e = std::getenv("GRPO_ROWS_LAUNCH");
-    if (e != nullptr) {
-      char* end = nullptr;
-      r.wg = int(std::strtol(e, &end, 10));
-      if (end != nullptr && *end == ',') r.unroll = int(std::strtol(end + 1, nullptr, 10));
-    }
-    return r;
-  }();
-  return o;
+inline LaunchOverride parse_launch(const char* e) {
+  LaunchOverride r;
+  if (e != nullptr) {
+    char* end = nullptr;
+    r.wg = int(std::strtol(e, &end, 10));
+    if (end != nullptr && *end == ',') r.unroll = int(std::strtol(end + 1, nullptr, 10));
+  }
+  return r;
+}
+inline LaunchOverride launch_override(int which) {
+  static const LaunchOverride both = parse_launch(std::getenv("GRPO_ROWS_LAUNCH"));
+  static const LaunchOverride fwd = parse_launch(std::getenv("GRPO_ROWS_FWD_LAUNCH"));
+  static const LaunchOverride bwd = parse_launch(std::getenv("GRPO_ROWS_BWD_LAUNCH"));
+  const LaunchOverride& o = which == 0 ? fwd : bwd;
+  return (o.wg > 0) ? o : both;
 }
 
 }  // namespace grpo

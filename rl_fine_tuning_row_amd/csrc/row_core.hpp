@@ -27,6 +27,18 @@ constexpr float kNegBig = -1e30f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming loads and stores.  NT selects the non-temporal form (the data is
+// not kept in the caches for reuse).  dlogits is written once and consumed by
+// another kernel, so its stores are non-temporal; logits loads are
+// non-temporal only when the host knows nothing re-reads them soon.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+__device__ __forceinline__ void store16(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -55,14 +67,14 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = to_bf16(
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* x) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
     x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
     x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
     x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
   }
-  __device__ __forceinline__ static uint4 pack(const float* x) {
-    uint4 v;
+  __device__ __forceinline__ static u32x4 pack(const float* x) {
+    u32x4 v;
     v.x = pack_bf16x2(x[0], x[1]);
     v.y = pack_bf16x2(x[2], x[3]);
     v.z = pack_bf16x2(x[4], x[5]);
@@ -72,12 +84,12 @@ template <> struct Vec<uint16_t> {
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
-  __device__ __forceinline__ static void unpack(const uint4& v, float* x) {
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* x) {
     x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
     x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
   }
-  __device__ __forceinline__ static uint4 pack(const float* x) {
-    uint4 v;
+  __device__ __forceinline__ static u32x4 pack(const float* x) {
+    u32x4 v;
     v.x = __float_as_uint(x[0]); v.y = __float_as_uint(x[1]);
     v.z = __float_as_uint(x[2]); v.w = __float_as_uint(x[3]);
     return v;

@@ -79,20 +79,20 @@ struct SeqArgs {
 // ---------------------------------------------------------------------------
 // forward: one pass over the row
 // ---------------------------------------------------------------------------
-template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T>
+template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
 __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, float c) {
   Stat st;
   stat_init(st);
   const int tid = threadIdx.x;
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
-    const uint4* __restrict__ rv = reinterpret_cast<const uint4*>(row);
+    const u32x4* __restrict__ rv = reinterpret_cast<const u32x4*>(row);
     const int nvec = V / VE;
     int i = tid;
     for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
-      uint4 v[UNROLL];
+      u32x4 v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) v[u] = rv[i + u * WG];
+      for (int u = 0; u < UNROLL; ++u) v[u] = load16<NTL>(rv + i + u * WG);
       float x[UNROLL * VE];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) Vec<TIn>::unpack(v[u], x + u * VE);
@@ -100,7 +100,7 @@ __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, flo
     }
     for (; i < nvec; i += WG) {
       float x[VE];
-      Vec<TIn>::unpack(rv[i], x);
+      Vec<TIn>::unpack(load16<NTL>(rv + i), x);
       stat_tile<VE, NEED_T>(st, x, c);
     }
     const int j = nvec * VE + tid;
@@ -125,12 +125,12 @@ __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, flo
   return st;
 }
 
-template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T>
+template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
 __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
   const int64_t r = blockIdx.x;
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
   const Stat st = block_reduce_stat<WG, NEED_T>(
-      scan_row<TIn, WG, UNROLL, VEC, NEED_T>(row, a.V, a.c), a.c);
+      scan_row<TIn, WG, UNROLL, VEC, NEED_T, NTL>(row, a.V, a.c), a.c);
   if (threadIdx.x != 0) return;
 
   const float logS = logf(st.s);
@@ -236,10 +236,10 @@ __device__ __forceinline__ void fill_row(TIn* __restrict__ out, int V, float val
     float x[VE];
 #pragma unroll
     for (int k = 0; k < VE; ++k) x[k] = value;
-    const uint4 pv = Vec<TIn>::pack(x);
-    uint4* __restrict__ ov = reinterpret_cast<uint4*>(out);
+    const u32x4 pv = Vec<TIn>::pack(x);
+    u32x4* __restrict__ ov = reinterpret_cast<u32x4*>(out);
     const int nvec = V / VE;
-    for (int i = threadIdx.x; i < nvec; i += WG) ov[i] = pv;
+    for (int i = threadIdx.x; i < nvec; i += WG) store16(ov + i, pv);
     const int j = nvec * VE + threadIdx.x;
     if (j < V) store_elem(out + j, value);
   } else {
@@ -271,15 +271,15 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   const int yi = int(y);
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
-    const uint4* rv = reinterpret_cast<const uint4*>(row);
-    uint4* ov = reinterpret_cast<uint4*>(out);
+    const u32x4* rv = reinterpret_cast<const u32x4*>(row);
+    u32x4* ov = reinterpret_cast<u32x4*>(out);
     const int nvec = a.V / VE;
     const int vy = yi / VE, ky = yi % VE;
     int i = threadIdx.x;
     for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
-      uint4 v[UNROLL];
+      u32x4 v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) v[u] = rv[i + u * WG];
+      for (int u = 0; u < UNROLL; ++u) v[u] = load16<false>(rv + i + u * WG);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         float x[VE];
@@ -291,12 +291,12 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
           for (int k = 0; k < VE; ++k)
             if (k == ky) x[k] += coef;
         }
-        ov[i + u * WG] = Vec<TIn>::pack(x);
+        store16(ov + i + u * WG, Vec<TIn>::pack(x));
       }
     }
     for (; i < nvec; i += WG) {
       float x[VE];
-      Vec<TIn>::unpack(rv[i], x);
+      Vec<TIn>::unpack(load16<false>(rv + i), x);
 #pragma unroll
       for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
       if (i == vy) {
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
         for (int k = 0; k < VE; ++k)
           if (k == ky) x[k] += coef;
       }
-      ov[i] = Vec<TIn>::pack(x);
+      store16(ov + i, Vec<TIn>::pack(x));
     }
     const int j = nvec * VE + threadIdx.x;
     if (j < a.V) {
@@ -328,14 +328,26 @@ struct Shape {
   int wg, unroll;
 };
 
-// default shapes: one workgroup per row; wider workgroups for longer rows
-inline Shape pick_shape(int64_t V, int es) {
-  const LaunchOverride o = launch_override();
+// Default launch shapes (one workgroup per row), from a sweep on MI355X:
+// the forward, which ends in a workgroup reduction, prefers one wave per row
+// when there are few rows (a few thousand) and 512 lanes otherwise; the
+// backward, which streams a read and a write, prefers 1024 lanes per row.
+inline Shape pick_fwd_shape(int64_t rows, int64_t V, int es) {
+  const LaunchOverride o = launch_override(0);
   if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
-  const int64_t bytes = V * es;
-  if (bytes <= 16 * 1024) return {256, 2};
-  if (bytes <= 128 * 1024) return {256, 4};
-  return {512, 4};
+  const int64_t nvec = V * es / 16;
+  if (nvec <= 512) return {64, 4};
+  if (rows <= 4096) return {64, 4};
+  return {512, 2};
+}
+
+inline Shape pick_bwd_shape(int64_t rows, int64_t V, int es) {
+  const LaunchOverride o = launch_override(1);
+  if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
+  const int64_t nvec = V * es / 16;
+  if (nvec <= 1024) return {256, 2};
+  (void)rows;
+  return {1024, 2};
 }
 
 #define GRPO_SHAPES(X) \
@@ -349,17 +361,17 @@ inline Shape pick_shape(int64_t V, int es) {
   X(1024, 2)           \
   X(1024, 4)
 
-template <typename TIn, bool VEC, bool NEED_T>
+template <typename TIn, bool VEC, bool NEED_T, bool NTL>
 hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_fwd_kernel<TIn, 256, 4, false, NEED_T>), dim3(unsigned(rows)),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL((row_fwd_kernel<TIn, 256, 4, false, NEED_T, false>),
+                       dim3(unsigned(rows)), dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
 #define X(W, U)                                                                          \
   if (sh.wg == W && sh.unroll == U) {                                                     \
-    hipLaunchKernelGGL((row_fwd_kernel<TIn, W, U, true, NEED_T>), dim3(unsigned(rows)),   \
-                       dim3(W), 0, s, a);                                                 \
+    hipLaunchKernelGGL((row_fwd_kernel<TIn, W, U, true, NEED_T, NTL>),                    \
+                       dim3(unsigned(rows)), dim3(W), 0, s, a);                           \
     return hipGetLastError();                                                             \
   }
     GRPO_SHAPES(X)
@@ -392,28 +404,36 @@ inline bool rows_vec_ok(const void* p, int64_t ld, int es) {
   return aligned(p, 16) && ((ld * es) % 16) == 0;
 }
 
+template <typename TIn>
+hipError_t launch_fwd_dt(const FwdArgs& a, int64_t rows, Shape sh, bool vec, bool need_t,
+                         bool ntl, hipStream_t s) {
+  if (!vec) return need_t ? launch_fwd_t<TIn, false, true, false>(a, rows, sh, s)
+                          : launch_fwd_t<TIn, false, false, false>(a, rows, sh, s);
+  if (need_t) return ntl ? launch_fwd_t<TIn, true, true, true>(a, rows, sh, s)
+                         : launch_fwd_t<TIn, true, true, false>(a, rows, sh, s);
+  return ntl ? launch_fwd_t<TIn, true, false, true>(a, rows, sh, s)
+             : launch_fwd_t<TIn, true, false, false>(a, rows, sh, s);
+}
+
+// Logits matrices larger than this are read with non-temporal loads by the
+// forward-type kernels: they cannot stay in the 256 MB last-level cache for
+// a following backward anyway, and streaming them past it measured faster.
+constexpr int64_t kNtLoadBytes = int64_t(192) << 20;
+
 int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s) {
   const int es = elem_size(dtype);
-  const Shape sh = pick_shape(a.V, es);
+  const Shape sh = pick_fwd_shape(rows, a.V, es);
   const bool vec = rows_vec_ok(a.logits, a.ld, es);
-  hipError_t e;
-  if (dtype == GRPO_BF16) {
-    if (vec) e = need_t ? launch_fwd_t<uint16_t, true, true>(a, rows, sh, s)
-                        : launch_fwd_t<uint16_t, true, false>(a, rows, sh, s);
-    else e = need_t ? launch_fwd_t<uint16_t, false, true>(a, rows, sh, s)
-                    : launch_fwd_t<uint16_t, false, false>(a, rows, sh, s);
-  } else {
-    if (vec) e = need_t ? launch_fwd_t<float, true, true>(a, rows, sh, s)
-                        : launch_fwd_t<float, true, false>(a, rows, sh, s);
-    else e = need_t ? launch_fwd_t<float, false, true>(a, rows, sh, s)
-                    : launch_fwd_t<float, false, false>(a, rows, sh, s);
-  }
+  const bool ntl = rows * a.ld * es > kNtLoadBytes;
+  const hipError_t e = dtype == GRPO_BF16
+                           ? launch_fwd_dt<uint16_t>(a, rows, sh, vec, need_t, ntl, s)
+                           : launch_fwd_dt<float>(a, rows, sh, vec, need_t, ntl, s);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
 int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
-  const Shape sh = pick_shape(a.V, es);
+  const Shape sh = pick_bwd_shape(rows, a.V, es);
   const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
   hipError_t e;
   if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, true>(a, rows, sh, s)
