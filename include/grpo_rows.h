@@ -211,8 +211,10 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  * loss_accum fp32 [1] (in/out, device); grad_hidden fp32 [R, H] (out);
  * grad_weight fp32 [V, H] (in/out)
  * workspace: device buffer of at least
- *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned.
- * H must be a multiple of 64 and at most 65536.
+ *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned; it
+ *   holds the chunk's fp32 logits and bf16 dlogits (about 6 R V bytes).
+ * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,
+ * weight and grad_hidden 16-byte aligned.  The result is deterministic.
  * ------------------------------------------------------------------------ */
 int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t H,
                             const void* weight, int64_t V, const int64_t* ids,
@@ -223,6 +225,21 @@ int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t
 
 /* Workspace bytes fused_linear_grpo_chunk needs for R rows (0 on bad sizes). */
 size_t fused_linear_grpo_workspace_bytes(int64_t rows, int64_t V, int64_t H);
+
+/* ------------------------------------------------------------------------
+ * grpo_gemm_bf16 -- the bf16 matrix-core product the fused-linear path is
+ * built from, exported on its own:  C[M, N] (=, or += with accumulate = 1)
+ *   sum_k A[m, k] B[k, n],  fp32 accumulation and output.
+ * a_layout 0: A[m, k] at A + m*lda + k (K-contiguous); 1: at A + k*lda + m.
+ * b_layout 0: B[k, n] at B + n*ldb + k (K-contiguous); 1: at B + k*ldb + n.
+ * A, B bf16, 16-byte aligned, lda and ldb multiples of 8; K, and M (N) when A
+ * (B) is not K-contiguous, multiples of 8.  C fp32 row-major with ldc >= N.
+ * [LIGER-TRL items 3-4: the chunk's logits h W^T and the gradients dz W and
+ *  dz^T h are these three products.]
+ * ------------------------------------------------------------------------ */
+int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const void* B, int b_layout,
+                   int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                   int accumulate, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* grpo_status_string(int status);

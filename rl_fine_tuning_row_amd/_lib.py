@@ -55,6 +55,7 @@ _SIGS = {
     "fused_linear_grpo_chunk": [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
                                 ctypes.POINTER(GrpoParams), _P, _P, _P, _P, ctypes.c_size_t, _P],
     "fused_linear_grpo_workspace_bytes": [_I64, _I64, _I64],
+    "grpo_gemm_bf16": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I64, _I64, _I64, _I, _P],
     "grpo_status_string": [_I],
 }
 _RESTYPE = {"fused_linear_grpo_workspace_bytes": ctypes.c_size_t,
@@ -325,3 +326,27 @@ def fused_linear_grpo_chunk(hidden, weight, ids, old_logp, adv, mask, dloss, nse
                                        _stream(stream))
     _check("fused_linear_grpo_chunk", st)
     return loss_accum, grad_hidden, grad_weight
+
+
+def grpo_gemm_bf16(A, B, *, a_layout=0, b_layout=0, M=None, N=None, K=None, C=None,
+                   accumulate=False, stream=None):
+    """C (fp32 [M, N]) = or += A B with bf16 A and B given as 2-D device tensors:
+    a_layout 0: A is [M, K]; 1: A is [K, M].  b_layout 0: B is [N, K]; 1: B is [K, N]."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B need unit column stride")
+    am, ak = (A.shape[0], A.shape[1]) if a_layout == 0 else (A.shape[1], A.shape[0])
+    bn, bk = (B.shape[0], B.shape[1]) if b_layout == 0 else (B.shape[1], B.shape[0])
+    if ak != bk:
+        raise ValueError(f"inner sizes differ: {ak} vs {bk}")
+    M, N, K = am, bn, ak
+    if C is None:
+        C = torch.zeros((M, N), dtype=torch.float32, device=A.device)
+    if C.dtype != torch.float32 or C.stride(1) != 1 or tuple(C.shape) != (M, N):
+        raise ValueError("C must be fp32 [M, N] with unit column stride")
+    st = lib().grpo_gemm_bf16(_ptr(A), a_layout, A.stride(0), _ptr(B), b_layout, B.stride(0),
+                              _ptr(C), C.stride(0), M, N, K, int(bool(accumulate)),
+                              _stream(stream))
+    _check("grpo_gemm_bf16", st)
+    return C

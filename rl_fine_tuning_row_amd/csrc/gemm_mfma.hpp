@@ -1,0 +1,52 @@
+// gemm_mfma.hpp -- bf16 x bf16 -> fp32 GEMM on gfx950 matrix cores.
+//
+// C[M, N] (=, += or split-K partial) = sum_k A[m, k] B[k, n].
+// A is either K-contiguous (A[m, k] at A + m*lda + k) or M-contiguous
+// (A + k*lda + m); B is either K-contiguous (B + n*ldb + k) or N-contiguous
+// (B + k*ldb + n).  The three products of the chunked fused-linear loss use
+// three of these layouts:
+//   logits       = h  W^T : A = h  [R, H]  K-contig, B = W [V, H] K-contig
+//   grad_hidden  = dz W   : A = dz [R, V]  K-contig, B = W [V, H] N-contig
+//   grad_weight += dz^T h : A = dz [R, V]  M-contig, B = h [R, H] N-contig
+//
+// Block tile 128 x 128 x 32, 256 lanes = 4 waves in a 2 x 2 grid, each wave
+// a 64 x 64 tile of 2 x 2 v_mfma_f32_32x32x16_bf16 (accumulators in
+// registers).  Tiles are staged global -> registers -> LDS, double buffered:
+// the next tile's global loads are in flight while the current one feeds
+// the MFMAs.  LDS rows are K-contiguous with a 16-byte pad, so each lane's
+// 8-element operand fragment is one conflict-free 128-bit LDS read.  A
+// non-K-contiguous operand is transposed while staged: each lane loads two
+// K-rows of an 8 x 8 block and writes 8 (k, k+1) pairs (one v_perm_b32 each).
+//
+// Operand fragment layout of v_mfma_f32_32x32x16_bf16 (checked on MI355X):
+// lane l holds A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32],
+// j = 0..7; accumulator i of lane l is D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace grpo {
+
+enum GemmMode : int32_t { GEMM_STORE = 0, GEMM_ACCUM = 1 };
+
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  float* C;
+  int64_t ldc;
+  int32_t M, N, K;
+  int32_t k_per_split;     // multiple of 32; split z covers [z*kps, min(K, (z+1)*kps))
+  int64_t split_stride;    // elements between the split-K partial slabs of C
+  int32_t tiles_m, tiles_n;
+};
+
+// Enqueue one GEMM; requires K, and the contiguous extent of every operand,
+// to be multiples of 8 (16-byte chunks), lda/ldb multiples of 8, 16-byte
+// aligned A and B.  splits > 1 writes partial sums to C + z * split_stride.
+hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g, int splits,
+                     hipStream_t s);
+
+}  // namespace grpo

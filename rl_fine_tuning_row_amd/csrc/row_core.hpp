@@ -28,6 +28,7 @@ constexpr float kNegBig = -1e30f;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Streaming loads and stores.  NT selects the non-temporal form (the data is
 // not kept in the caches for reuse).  dlogits is written once and consumed by

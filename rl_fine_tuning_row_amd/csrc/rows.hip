@@ -16,65 +16,9 @@
 #include "grpo_rows.h"
 #include "host_common.hpp"
 #include "row_core.hpp"
+#include "rows_internal.hpp"
 
 namespace grpo {
-
-enum FwdMode : int32_t { FWD_GRPO = 0, FWD_ENTROPY = 1, FWD_LSM = 2 };
-enum BwdMode : int32_t { BWD_GRPO = 0, BWD_LSM = 1 };
-
-struct FwdArgs {
-  const void* logits;
-  int64_t ld;
-  int32_t V;
-  int32_t L;  // tokens per sequence (GRPO); 1 otherwise
-  const int64_t* ids;
-  const float* old_logp;
-  const float* ref_logp;
-  const float* adv;
-  float T, c, beta, lo, hi;
-  int32_t mode, level;
-  float* loss;
-  float* logp;
-  float* lse;
-  float* entropy;
-  float* kl;
-  uint8_t* is_clipped;
-  float* gathered;
-  int32_t* err_count;
-};
-
-struct BwdArgs {
-  const void* logits;
-  int64_t ld;
-  void* dlogits;
-  int64_t ld_out;
-  int32_t V;
-  int32_t L;
-  const int64_t* ids;
-  const float* old_logp;
-  const float* ref_logp;
-  const float* adv;
-  const uint8_t* mask;
-  const float* logp;
-  const float* lse;
-  const float* seq_ratio;
-  const float* dloss;  // grad_logp in BWD_LSM mode
-  float T, c, beta, lo, hi;
-  int32_t mode, level, force_dense;
-  uint8_t* zero_row;
-};
-
-struct SeqArgs {
-  int32_t L;
-  const float* logp;
-  const float* old_logp;
-  const uint8_t* mask;
-  const float* adv;
-  float lo, hi;
-  float* loss;
-  uint8_t* is_clipped;
-  float* seq_ratio;
-};
 
 // ---------------------------------------------------------------------------
 // forward: one pass over the row
@@ -229,17 +173,26 @@ __device__ __forceinline__ float row_dlogp(const BwdArgs& a, int64_t r) {
   return coef * ws * m / n + klg * w;
 }
 
-template <typename TIn, int WG, bool VEC>
-__device__ __forceinline__ void fill_row(TIn* __restrict__ out, int V, float value) {
+// store VE = Vec<TIn>::N results as one vector of the output dtype
+template <typename TIn, typename TOut>
+__device__ __forceinline__ void store_vec(TOut* __restrict__ out, int i, const float* x) {
+  if constexpr (sizeof(TIn) == sizeof(TOut)) {
+    store16(reinterpret_cast<u32x4*>(out) + i, Vec<TIn>::pack(x));
+  } else {  // 4 fp32 results -> 4 bf16 (8 bytes)
+    const u32x2 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(out) + i);
+  }
+}
+
+template <typename TIn, typename TOut, int WG, bool VEC>
+__device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float value) {
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
     float x[VE];
 #pragma unroll
     for (int k = 0; k < VE; ++k) x[k] = value;
-    const u32x4 pv = Vec<TIn>::pack(x);
-    u32x4* __restrict__ ov = reinterpret_cast<u32x4*>(out);
     const int nvec = V / VE;
-    for (int i = threadIdx.x; i < nvec; i += WG) store16(ov + i, pv);
+    for (int i = threadIdx.x; i < nvec; i += WG) store_vec<TIn, TOut>(out, i, x);
     const int j = nvec * VE + threadIdx.x;
     if (j < V) store_elem(out + j, value);
   } else {
@@ -247,21 +200,21 @@ __device__ __forceinline__ void fill_row(TIn* __restrict__ out, int V, float val
   }
 }
 
-template <typename TIn, int WG, int UNROLL, bool VEC>
+template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC>
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   const int64_t r = blockIdx.x;
   const float g = uniform(row_dlogp<TIn, WG>(a, r));
   const int64_t y = a.ids[r];
   const bool valid = y >= 0 && y < a.V;
-  TIn* __restrict__ out = static_cast<TIn*>(a.dlogits) + r * a.ld_out;
+  TOut* __restrict__ out = static_cast<TOut*>(a.dlogits) + r * a.ld_out;
   const bool zero = (g == 0.0f);
   if (threadIdx.x == 0 && a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
   if (!valid) {
-    fill_row<TIn, WG, false>(out, a.V, __builtin_nanf(""));
+    fill_row<TIn, TOut, WG, false>(out, a.V, __builtin_nanf(""));
     return;
   }
   if (zero && !a.force_dense) {  // early path: no logits read, no exp
-    fill_row<TIn, WG, VEC>(out, a.V, 0.0f);
+    fill_row<TIn, TOut, WG, VEC>(out, a.V, 0.0f);
     return;
   }
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
@@ -272,7 +225,6 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
     const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-    u32x4* ov = reinterpret_cast<u32x4*>(out);
     const int nvec = a.V / VE;
     const int vy = yi / VE, ky = yi % VE;
     int i = threadIdx.x;
@@ -291,7 +243,7 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
           for (int k = 0; k < VE; ++k)
             if (k == ky) x[k] += coef;
         }
-        store16(ov + i + u * WG, Vec<TIn>::pack(x));
+        store_vec<TIn, TOut>(out, i + u * WG, x);
       }
     }
     for (; i < nvec; i += WG) {
@@ -304,7 +256,7 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
         for (int k = 0; k < VE; ++k)
           if (k == ky) x[k] += coef;
       }
-      store16(ov + i, Vec<TIn>::pack(x));
+      store_vec<TIn, TOut>(out, i, x);
     }
     const int j = nvec * VE + threadIdx.x;
     if (j < a.V) {
@@ -380,18 +332,18 @@ hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s)
   }
 }
 
-template <typename TIn, bool VEC>
+template <typename TIn, typename TOut, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, 256, 4, false>), dim3(unsigned(rows)), dim3(256),
-                       0, s, a);
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false>), dim3(unsigned(rows)),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
-#define X(W, U)                                                                           \
-  if (sh.wg == W && sh.unroll == U) {                                                      \
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, W, U, true>), dim3(unsigned(rows)), dim3(W), 0, \
-                       s, a);                                                              \
-    return hipGetLastError();                                                              \
+#define X(W, U)                                                                          \
+  if (sh.wg == W && sh.unroll == U) {                                                     \
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true>), dim3(unsigned(rows)),     \
+                       dim3(W), 0, s, a);                                                 \
+    return hipGetLastError();                                                             \
   }
     GRPO_SHAPES(X)
 #undef X
@@ -436,9 +388,20 @@ int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   const Shape sh = pick_bwd_shape(rows, a.V, es);
   const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
   hipError_t e;
-  if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, true>(a, rows, sh, s)
-                                  : launch_bwd_t<uint16_t, false>(a, rows, sh, s);
-  else e = vec ? launch_bwd_t<float, true>(a, rows, sh, s) : launch_bwd_t<float, false>(a, rows, sh, s);
+  if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, uint16_t, true>(a, rows, sh, s)
+                                  : launch_bwd_t<uint16_t, uint16_t, false>(a, rows, sh, s);
+  else e = vec ? launch_bwd_t<float, float, true>(a, rows, sh, s)
+               : launch_bwd_t<float, float, false>(a, rows, sh, s);
+  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s) {
+  const Shape sh = pick_bwd_shape(rows, a.V, 4);
+  // fp32 rows in 16-byte vectors, bf16 rows in 8-byte vectors
+  const bool vec = rows_vec_ok(a.logits, a.ld, 4) && aligned(a.dlogits, 8) &&
+                   ((a.ld_out * 2) % 8) == 0;
+  const hipError_t e = vec ? launch_bwd_t<float, uint16_t, true>(a, rows, sh, s)
+                           : launch_bwd_t<float, uint16_t, false>(a, rows, sh, s);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 

@@ -1,0 +1,75 @@
+// rows_internal.hpp -- argument blocks and launchers of the row kernels,
+// shared by the C ABI entry points and the fused-linear path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace grpo {
+
+enum FwdMode : int32_t { FWD_GRPO = 0, FWD_ENTROPY = 1, FWD_LSM = 2 };
+enum BwdMode : int32_t { BWD_GRPO = 0, BWD_LSM = 1 };
+
+struct FwdArgs {
+  const void* logits;
+  int64_t ld;
+  int32_t V;
+  int32_t L;  // tokens per sequence (GRPO); 1 otherwise
+  const int64_t* ids;
+  const float* old_logp;
+  const float* ref_logp;
+  const float* adv;
+  float T, c, beta, lo, hi;
+  int32_t mode, level;
+  float* loss;
+  float* logp;
+  float* lse;
+  float* entropy;
+  float* kl;
+  uint8_t* is_clipped;
+  float* gathered;
+  int32_t* err_count;
+};
+
+struct BwdArgs {
+  const void* logits;
+  int64_t ld;
+  void* dlogits;
+  int64_t ld_out;
+  int32_t V;
+  int32_t L;
+  const int64_t* ids;
+  const float* old_logp;
+  const float* ref_logp;
+  const float* adv;
+  const uint8_t* mask;
+  const float* logp;
+  const float* lse;
+  const float* seq_ratio;
+  const float* dloss;  // grad_logp in BWD_LSM mode
+  float T, c, beta, lo, hi;
+  int32_t mode, level, force_dense;
+  uint8_t* zero_row;
+};
+
+struct SeqArgs {
+  int32_t L;
+  const float* logp;
+  const float* old_logp;
+  const uint8_t* mask;
+  const float* adv;
+  float lo, hi;
+  float* loss;
+  uint8_t* is_clipped;
+  float* seq_ratio;
+};
+
+// Launch the forward-type row kernel (GRPO / entropy / selective
+// log-softmax, by a.mode) over `rows` rows of `dtype` logits.
+int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s);
+// Launch the backward row kernel; logits and dlogits of the same dtype.
+int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s);
+// Backward row kernel over fp32 logits writing bf16 dlogits.
+int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s);
+
+}  // namespace grpo

@@ -362,3 +362,8 @@ def stored_check_rows(name: str):
     import json
     with open(os.path.join(_GOLDEN, f"oracle_logp_{name}.json")) as f:
         return json.load(f)["check_rows"]
+
+
+def load_stored_lse(name: str) -> np.ndarray:
+    """float64 [B*L] row log-sum-exp stored beside ``load_stored_logp``."""
+    return np.load(os.path.join(_GOLDEN, f"oracle_lse_{name}.npy"))

@@ -6,7 +6,7 @@ The GRPO workloads form old_logp and ref_logp as the policy's own logp plus
 noise.  That logp is the oracle's (float64, on the bf16-rounded logits; for
 the fused workload on the logits h W^T of the bf16 hidden states and weight).
 This script calls only ``oracle/`` and ``synth/`` and stores, per workload,
-``oracle_logp_<name>.npy`` (float64 [B*L]) plus the bit patterns of a few
+``oracle_logp_<name>.npy`` and ``oracle_lse_<name>.npy`` (float64 [B*L]) plus a digest of the bit patterns of a few
 logits rows in ``oracle_logp_<name>.json`` so a loader can check that the
 generators still produce the same inputs.
 """
@@ -37,15 +37,16 @@ def row_digest(rows: np.ndarray) -> str:
 
 def blocked_logp(z_bits_or_none, get_block, n_rows, ids, T, block=128, threads=8):
     out = np.empty(n_rows, np.float64)
+    lse = np.empty(n_rows, np.float64)
 
     def job(r0):
         r1 = min(n_rows, r0 + block)
         z = get_block(r0, r1)
-        out[r0:r1] = oracle.selective_log_softmax(z, ids[r0:r1], T)[0]
+        out[r0:r1], lse[r0:r1] = oracle.selective_log_softmax(z, ids[r0:r1], T)
 
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(job, range(0, n_rows, block)))
-    return out
+    return out, lse
 
 
 def make_grpo(case: synth.GrpoCase, name: str):
@@ -55,12 +56,12 @@ def make_grpo(case: synth.GrpoCase, name: str):
     def get_block(r0, r1):
         return oracle.decode_bf16(z[r0:r1])
 
-    logp = blocked_logp(None, get_block, case.N, case.ids, case.temperature)
+    logp, lse = blocked_logp(None, get_block, case.N, case.ids, case.temperature)
     meta = {"name": name, "case": case.name, "rows": case.N, "V": case.V,
             "check_rows": list(CHECK_ROWS),
             "check_digest": row_digest(z[list(CHECK_ROWS)]),
-            "note": "oracle float64 logp of the bf16 logits at the workload's temperature"}
-    return logp, meta, time.time() - t0
+            "note": "oracle float64 logp and lse of the bf16 logits at the workload's temperature"}
+    return (logp, lse), meta, time.time() - t0
 
 
 def make_fused(case: synth.FusedCase, name: str):
@@ -72,18 +73,20 @@ def make_fused(case: synth.FusedCase, name: str):
     def get_block(r0, r1):
         return h[r0:r1] @ Wt
 
-    logp = blocked_logp(None, get_block, case.N, case.ids, case.temperature, block=256,
-                        threads=2)
+    logp, lse = blocked_logp(None, get_block, case.N, case.ids, case.temperature, block=256,
+                             threads=2)
     meta = {"name": name, "case": case.name, "rows": case.N, "V": case.V, "H": case.H,
             "check_rows": list(CHECK_ROWS),
             "check_digest": row_digest(case.hidden[list(CHECK_ROWS)]) + ":" +
             row_digest(case.weight[list(CHECK_ROWS)]),
-            "note": "oracle float64 logp of h W^T (bf16 h and W) at the workload's temperature"}
-    return logp, meta, time.time() - t0
+            "note": "oracle float64 logp and lse of h W^T (bf16 h and W) at the workload's temperature"}
+    return (logp, lse), meta, time.time() - t0
 
 
-def save(name, logp, meta):
+def save(name, logp_lse, meta):
+    logp, lse = logp_lse
     np.save(os.path.join(HERE, f"oracle_logp_{name}.npy"), logp)
+    np.save(os.path.join(HERE, f"oracle_lse_{name}.npy"), lse)
     with open(os.path.join(HERE, f"oracle_logp_{name}.json"), "w") as f:
         json.dump(meta, f, indent=1)
 
