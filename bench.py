@@ -1,29 +1,40 @@
 """Benchmark of the GRPO logits row pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--sets S] [--chunk C] [--no-cpu-baseline] [--copy-probe]
 
-A step is one forward + backward of the token-level GRPO loss over the
-logits of B=4 sequences x L=512 tokens x V=32000 vocabulary entries (bf16,
-T=0.9, beta=0.04, eps 0.2/0.28, half the advantages exactly 0, no reference
-model so the KL term vanishes, token-mean upstream gradient):
-grpo_logits_fwd writes loss, logp, lse, entropy, kl and is_clipped per token;
-grpo_logits_bwd writes dlogits with the all-zero path on rows whose dlogp is 0.
-Inputs are synthetic and already resident in device memory; S input/output
-buffer sets (about 1 GB in total by default) rotate from step to step so a
-step does not find the previous step's logits in the 256 MB last-level cache.
+Default workload ``grpo-token`` (the headline): a step is one forward +
+backward of the token-level GRPO loss over the logits of B=4 sequences x
+L=512 tokens x V=32000 vocabulary entries (bf16, T=0.9, beta=0.04, eps
+0.2/0.28, half the advantages exactly 0, no reference model so the KL term
+vanishes, token-mean upstream gradient): grpo_logits_fwd writes loss, logp,
+lse, entropy, kl and is_clipped per token; grpo_logits_bwd writes dlogits,
+with the all-zero path on rows whose dlogp is 0.  S buffer sets (about 1 GB
+in total by default) rotate from step to step so a step does not find the
+previous step's logits in the 256 MB last-level cache.
 
-Prints one JSON line.  `value` is GB/s of algorithmic HBM bytes (logits read
-by the forward, logits re-read by the backward on its non-zero rows, dlogits
-written, plus the per-row scalars) over the wall time of the timed steps.
-`roofline` is for the dominant kernel, timed with events on its stream.
-`cpu_baseline` times the float64 oracle on the same workload on the host.
+Other workloads (each prints its own line; not the headline):
+  grpo-seq      sequence-level fwd+bwd, B=8 L=1024 V=151936 bf16, beta=0
+  rows          entropy_from_logits + selective_log_softmax fwd + bwd,
+                65536 x 32000 bf16 (contiguous; --strided: rows of a 2V buffer)
+  fused-linear  chunked fused-linear loss over h [32768, 1024] and
+                W [151936, 1024] bf16, --chunk sequences per call
+
+Inputs are synthetic, generated on the host and already resident in device
+memory when the timed region starts.  ``value`` is GB/s of algorithmic HBM
+bytes (TFLOP/s of the three products for fused-linear) over the wall time of
+the timed steps.  ``roofline`` is for the step's dominant kernel, its
+duration timed with events on the launch stream over back-to-back launches; ``traffic`` is the HBM bytes
+per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored in
+profiles/counters.json, used only while the kernels' source digest matches.
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on the host.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
-import platform
 import sys
 import time
 
@@ -32,7 +43,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
 
 
 def parse():
@@ -40,22 +52,78 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="grpo-token",
+                    choices=["grpo-token", "grpo-seq", "rows", "fused-linear"])
     ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--chunk", type=int, default=4)
+    ap.add_argument("--strided", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of 256 MiB (counter calibration)")
     return ap.parse_args()
 
 
-def per_row_bytes_fwd():
-    # ids int64, old_logp f32, adv (per sequence, negligible); out: loss, logp,
-    # lse, entropy, kl f32 + is_clipped u8
-    return 8 + 4 + 5 * 4 + 1
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
-def per_row_bytes_bwd():
-    # ids, old_logp, logp, lse, dloss in; zero_row out
-    return 8 + 4 + 4 + 4 + 4 + 1
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the stored counter runs, if the kernels have
+    not changed since (source digest)."""
+    from rl_fine_tuning_row_amd.build import source_digest
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_digest") != source_digest():
+        return None
+    e = data.get("kernels", {}).get(f"{workload}:{kernel}")
+    if e is None:
+        return None
+    return e["fetch_bytes"] + e["write_bytes"]
+
+
+def timed(step_fns, steps, torch):
+    """Wall time (ms) per step of `steps` steps rotating over step_fns."""
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step_fns[i % len(step_fns)]()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def kernel_times(launch_lists, steps, torch):
+    """Average duration (ms) of each launch position of a step: that launch
+    alone, `steps` times back to back (rotating over the buffer sets), between
+    two events on the launch stream.  Inputs of every position were produced
+    by the warm-up steps and no launch changes another's inputs."""
+    out = []
+    for k in range(len(launch_lists[0])):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            launch_lists[i % len(launch_lists)][k]()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
 
 
 def copy_probe(torch):
@@ -69,41 +137,274 @@ def copy_probe(torch):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(case, old):
-    """The float64 oracle on the whole workload (one step), timed on the host."""
+def base_line(args, metric, value, unit, ms, config, dtype="bf16"):
+    return {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config}
+
+
+# per-row scalar bytes of the GRPO kernels
+FWD_ROW_BYTES = 8 + 4 + 5 * 4 + 1      # ids, old_logp in; loss, logp, lse, entropy, kl, is_clipped out
+BWD_ROW_BYTES = 8 + 4 + 4 + 4 + 4 + 1  # ids, old_logp, logp, lse, dloss in; zero_row out
+
+
+# ---------------------------------------------------------------------------
+# GRPO token / sequence level
+# ---------------------------------------------------------------------------
+def run_grpo(args, torch, grl, synth, level):
+    if level == "token":
+        case = synth.grpo_token_case(with_ref=False, dloss="mean")
+        name = "token"
+    else:
+        case = synth.grpo_sequence_case(dloss="mean")
+        name = "sequence"
+    logp_true = synth.load_stored_logp(name, case.logits[synth.stored_check_rows(name)])
+    old = synth.add_noise_f32(logp_true, case.old_noise)
+    B, L, V, N = case.B, case.L, case.V, case.N
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    z0 = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    ids, old_t, adv, mask, dloss = (dev(case.ids), dev(old), dev(case.adv), dev(case.mask),
+                                    dev(case.dloss))
+    nsets = args.sets if level == "token" else 2
+    kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+              eps_high=case.eps_high, level=level)
+    sets = []
+    for k in range(nsets):
+        z = z0.clone() if k else z0
+        out = {n: torch.empty(N, dtype=torch.float32, device="cuda")
+               for n in ("loss", "logp", "lse", "entropy", "kl")}
+        out["is_clipped"] = torch.empty(N, dtype=torch.uint8, device="cuda")
+        dz = torch.empty((N, V), dtype=torch.bfloat16, device="cuda")
+        zr = torch.empty(N, dtype=torch.uint8, device="cuda")
+        # arguments marshalled once; a step is two C calls
+        fwd, out = grl.grpo_logits_fwd(z, ids, old_t, adv, B, L, mask=mask, out=out,
+                                       prepare=True, **kw)
+        bwd, _, _ = grl.grpo_logits_bwd(z, ids, old_t, adv, B, L, out["logp"], out["lse"],
+                                        dloss, mask=mask, seq_ratio=out.get("seq_ratio"),
+                                        dlogits=dz, zero_row=zr, prepare=True, **kw)
+        sets.append(dict(fwd=fwd, bwd=bwd, zr=zr))
+    steps = [(lambda s=s: (s["fwd"](), s["bwd"]())) for s in sets]
+    for i in range(args.warmup):
+        steps[i % len(steps)]()
+    torch.cuda.synchronize()
+    n_zero = int(sets[0]["zr"].sum().item())
+    n_nz = N - n_zero
+    ms = timed(steps, args.steps, torch)
+    fwd_ms, bwd_ms = kernel_times([[s["fwd"], s["bwd"]] for s in sets], args.steps, torch)
+    fwd_bytes = N * V * 2 + N * FWD_ROW_BYTES
+    bwd_bytes = N * V * 2 + n_nz * V * 2 + N * BWD_ROW_BYTES
+    step_bytes = fwd_bytes + bwd_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    kern = {"grpo_fwd": (fwd_ms, fwd_bytes), "grpo_bwd": (bwd_ms, bwd_bytes)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_gbs = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e9
+    wl = "grpo-token" if level == "token" else "grpo-seq"
+    if level == "token":
+        metric = "GRPO logits fwd+bwd GB/s & % HBM peak at B4 L512 V32000 bf16; rows/s"
+        desc = ("token-level GRPO logits fwd+bwd, B=4 L=512 V=32000 bf16 (T=0.9, beta=0.04, "
+                "eps 0.2/0.28, 2 of 4 advantages 0, ref = policy, token-mean dloss, "
+                "lengths U{256..512})")
+    else:
+        metric = "GRPO sequence-level logits fwd+bwd GB/s at B8 L1024 V151936 bf16; rows/s"
+        desc = ("sequence-level GRPO logits fwd+bwd, B=8 L=1024 V=151936 bf16 (T=1, beta=0, "
+                "eps 0.2/0.28, 2 of 8 advantages 0, one old-logp offset per sequence)")
+    res = base_line(args, metric, gbs, "GB/s", ms,
+                    {"workload": desc, "rows": N, "V": V, "zero_rows": n_zero,
+                     "nonzero_rows": n_nz, "buffer_sets": nsets, "accumulate": "fp32"})
+    res.update({
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(N / (ms * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "kernels": {k: {"ms": round(v[0], 5), "bytes": v[1],
+                        "GB/s": round(v[1] / (v[0] * 1e-3) / 1e9, 1)} for k, v in kern.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(dom, wl)},
+    })
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_grpo(case, old, level)
+    return res
+
+
+def cpu_grpo(case, old, level):
+    """The float64 oracle on the GRPO workload: whole steps for the headline,
+    whole sequences for the sequence level, until about 10 s of CPU work."""
     import oracle
-    R = case.N
-    reps = 0
-    t0 = time.perf_counter()
-    while True:   # whole steps until about 10 s of CPU work (at most 30 steps)
-        z = oracle.decode_bf16(case.logits)
-        fwd = oracle.grpo_forward(z, case.ids, old.astype(np.float64), None, case.adv,
-                                  case.mask, case.B, case.L, case.temperature, case.beta,
-                                  case.eps_low, case.eps_high)
-        dz, g, zr = oracle.grpo_backward(z, case.ids, old.astype(np.float64), None, case.adv,
-                                         case.mask, case.dloss, case.B, case.L,
-                                         case.temperature, case.beta, case.eps_low,
-                                         case.eps_high, fwd=fwd)
+    B = case.B if level == "token" else 1
+    R = B * case.L
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        z = oracle.decode_bf16(case.logits[:R])
+        a = dict(z=z, ids=case.ids[:R], old_logp=old[:R].astype(np.float64), ref_logp=None,
+                 adv=case.adv[:B], mask=case.mask[:R], B=B, L=case.L,
+                 temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+                 eps_high=case.eps_high, level=level)
+        fwd = oracle.grpo_forward(**a)
+        dz, g, zr = oracle.grpo_backward(dloss=case.dloss[:R], fwd=fwd, **a)
         reps += 1
         if time.perf_counter() - t0 > 10.0 or reps >= 30:
             break
     dt = (time.perf_counter() - t0) / reps
     nz = int((~zr).sum())
-    nbytes = (R * case.V * 2 + R * per_row_bytes_fwd()
-              + R * case.V * 2 + nz * case.V * 2 + R * per_row_bytes_bwd())
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    nbytes = R * case.V * 4 + nz * case.V * 2 + R * (FWD_ROW_BYTES + BWD_ROW_BYTES)
+    what = "full steps" if level == "token" else "single sequences"
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full steps (fwd+bwd, {R} rows x {case.V} each) in float64 "
-                      f"NumPy, {dt:.3f} s per step, single thread; {R / dt:.0f} rows/s; "
-                      f"host CPU {cpu}"}
+            "sample": f"{reps} {what} (fwd+bwd, {R} rows x {case.V}) in float64 NumPy, "
+                      f"{dt:.3f} s each, single thread; {R / dt:.0f} rows/s; host CPU {cpu_model()}"}
+
+
+# ---------------------------------------------------------------------------
+# entropy + selective log-softmax
+# ---------------------------------------------------------------------------
+def run_rows(args, torch, grl, synth):
+    case = synth.row_case()
+    N, V = case.N, case.V
+    z = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    if args.strided:
+        buf = torch.empty((N, 2 * V), dtype=torch.bfloat16, device="cuda")
+        buf[:, V:] = float("nan")
+        buf[:, :V] = z
+        del z
+        z = buf[:, :V]
+    ids = torch.from_numpy(case.ids).cuda()
+    grad = torch.from_numpy(case.grad).cuda()
+    H = torch.empty(N, device="cuda")
+    lp = torch.empty(N, device="cuda")
+    lse = torch.empty(N, device="cuda")
+    dz = torch.empty((N, V), dtype=torch.bfloat16, device="cuda")
+    L = grl.lib()
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ld = z.stride(0)
+
+    def chk(st):
+        if st != 0:
+            raise grl.GrpoError("rows", st)
+    f_ent = lambda: chk(L.entropy_from_logits(P(z), 1, N, V, ld, 1.0, P(H), s))
+    f_lsm = lambda: chk(L.selective_log_softmax(P(z), 1, N, V, ld, P(ids), 1.0, P(lp), P(lse), s))
+    f_bwd = lambda: chk(L.selective_log_softmax_bwd(P(z), 1, N, V, ld, P(ids), 1.0, P(lse), P(grad),
+                                                    P(dz), V, s))
+    launches = [f_ent, f_lsm, f_bwd]
+    step = lambda: [f() for f in launches]
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 20))
+    args.steps = steps
+    ms = timed([step], steps, torch)
+    kt = kernel_times([launches], steps, torch)
+    kb = [N * V * 2, N * V * 2, 2 * N * V * 2]
+    names = ["entropy", "lsm_fwd", "lsm_bwd"]
+    step_bytes = sum(kb) + N * (4 + 8 + 8 + 8 + 4)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    k = int(np.argmax(kt))
+    res = base_line(args, "entropy + selective log-softmax fwd+bwd GB/s at 65536x32000 bf16",
+                    gbs, "GB/s", ms,
+                    {"workload": "entropy_from_logits + selective_log_softmax fwd + bwd, N=65536 "
+                                 "(B16 L4096) V=32000 bf16, N(0,3^2) + 8 peak" +
+                                 (", rows of a [N, 2V] buffer" if args.strided else ""),
+                     "rows": N, "V": V, "row_stride": ld})
+    res.update({
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "kernels": {n: {"ms": round(t, 4), "GB/s": round(b / (t * 1e-3) / 1e9, 1)}
+                    for n, t, b in zip(names, kt, kb)},
+        "roofline": {"kernel": names[k], "bound": "hbm",
+                     "achieved": round(kb[k] / (kt[k] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kb[k] / (kt[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(names[k], "rows")},
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        R = 512
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            zz = oracle.decode_bf16(case.logits[:R])
+            oracle.entropy_from_logits(zz)
+            oracle.selective_log_softmax(zz, case.ids[:R])
+            oracle.selective_log_softmax_bwd(zz, case.ids[:R], case.grad[:R])
+            reps += 1
+            if time.perf_counter() - t0 > 10.0 or reps >= 30:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": R * V * 8 / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} x {R} rows (entropy, selective fwd, bwd) in "
+                                         f"float64 NumPy, {dt:.3f} s each, single thread; host "
+                                         f"CPU {cpu_model()}"}
+    return res
+
+
+# ---------------------------------------------------------------------------
+# chunked fused-linear
+# ---------------------------------------------------------------------------
+def run_fused(args, torch, grl, synth):
+    case = synth.fused_case(dloss="mean")
+    rows = synth.stored_check_rows("fused")
+    lp = synth.load_stored_logp("fused", case.hidden[rows])
+    old = synth.add_noise_f32(lp, case.old_noise)
+    ref = synth.add_noise_f32(lp, case.ref_noise)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    h = torch.from_numpy(case.hidden.view(np.int16)).view(torch.bfloat16).cuda()
+    W = torch.from_numpy(case.weight.view(np.int16)).view(torch.bfloat16).cuda()
+    ids, old_t, ref_t, adv, mask, dl = (dev(case.ids), dev(old), dev(ref), dev(case.adv),
+                                        dev(case.mask), dev(case.dloss))
+    c = args.chunk
+    loss = torch.zeros(1, device="cuda")
+    gW = torch.zeros((case.V, case.H), device="cuda")
+    gh = torch.empty((case.N, case.H), device="cuda")
+    ws = torch.empty(grl.fused_linear_grpo_workspace_bytes(c * case.L, case.V, case.H),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+              eps_high=case.eps_high)
+    calls = []
+    for b0 in range(0, case.B, c):
+        nb = min(c, case.B - b0)
+        rs = slice(b0 * case.L, (b0 + nb) * case.L)
+        calls.append(lambda rs=rs, b0=b0, nb=nb: grl.fused_linear_grpo_chunk(
+            h[rs], W, ids[rs], old_t[rs], adv[b0:b0 + nb], mask[rs], dl[rs], nb, case.L,
+            ref_logp=ref_t[rs], loss_accum=loss, grad_hidden=gh[rs], grad_weight=gW,
+            workspace=ws, **kw))
+    step = lambda: [f() for f in calls]
+    for _ in range(max(1, min(args.warmup, 3))):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 5))
+    args.steps = steps
+    ms = timed([step], steps, torch)
+    flops = 3 * 2.0 * case.N * case.V * case.H
+    tfs = flops / (ms * 1e-3) / 1e12
+    res = base_line(args, "chunked fused-linear GRPO fwd+bwd TFLOP/s (3 GEMMs) at B32 L1024 "
+                          "H1024 V151936 bf16", tfs, "TFLOP/s", ms,
+                    {"workload": f"fused-linear GRPO, h [32768, 1024] x W [151936, 1024] bf16, "
+                                 f"{c} sequences per chunk, T=0.9 beta=0.04",
+                     "chunk_sequences": c, "workspace_bytes": ws.numel(),
+                     "full_logits_fp32_bytes": case.N * case.V * 4})
+    res.update({
+        "pct_mfma_peak": round(100.0 * tfs / MFMA_BF16_PEAK_TFS, 2),
+        "roofline": {"kernel": "whole chunk loop (GEMM flops over all time)", "bound": "mfma",
+                     "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        hh = oracle.decode_bf16(case.hidden[:case.L])
+        WW = oracle.decode_bf16(case.weight)
+        t0 = time.perf_counter()
+        oracle.fused_linear_grpo(hh, WW, case.ids[:case.L], old[:case.L].astype(np.float64),
+                                 ref[:case.L].astype(np.float64), case.adv[:1],
+                                 case.mask[:case.L], case.dloss[:case.L], 1, case.L,
+                                 case.temperature, case.beta, case.eps_low, case.eps_high, 1)
+        dt = time.perf_counter() - t0
+        cores = len(os.sched_getaffinity(0))
+        res["cpu_baseline"] = {"value": 3 * 2.0 * case.L * case.V * case.H / dt / 1e12,
+                               "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "sample": f"one sequence (1024 rows) of the fused-linear loss in "
+                                         f"float64 NumPy/BLAS, {dt:.2f} s; up to {cores} BLAS "
+                                         f"threads; host CPU {cpu_model()}"}
+    return res
 
 
 def main():
@@ -124,112 +425,14 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
         return
-
-    case = synth.grpo_token_case(with_ref=False, dloss="mean")
-    logp_true = synth.load_stored_logp("token", case.logits[synth.stored_check_rows("token")])
-    old = synth.add_noise_f32(logp_true, case.old_noise)
-    B, L, V, N = case.B, case.L, case.V, case.N
-
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    z0 = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
-    ids, old_t, adv, mask, dloss = dev(case.ids), dev(old), dev(case.adv), dev(case.mask), dev(case.dloss)
-    sets = []
-    for k in range(args.sets):
-        z = z0.clone() if k else z0
-        out = {n: torch.empty(N, dtype=torch.float32, device="cuda")
-               for n in ("loss", "logp", "lse", "entropy", "kl")}
-        out["is_clipped"] = torch.empty(N, dtype=torch.uint8, device="cuda")
-        sets.append(dict(z=z, out=out, dz=torch.empty((N, V), dtype=torch.bfloat16, device="cuda"),
-                         zr=torch.empty(N, dtype=torch.uint8, device="cuda")))
-    kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
-              eps_high=case.eps_high, level="token")
-
-    # arguments are marshalled once per buffer set; a step is two C calls
-    for s in sets:
-        s["fwd"], _ = grl.grpo_logits_fwd(s["z"], ids, old_t, adv, B, L, mask=mask,
-                                          out=s["out"], prepare=True, **kw)
-        s["bwd"], _, _ = grl.grpo_logits_bwd(s["z"], ids, old_t, adv, B, L, s["out"]["logp"],
-                                             s["out"]["lse"], dloss, mask=mask, dlogits=s["dz"],
-                                             zero_row=s["zr"], prepare=True, **kw)
-
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
-        s["fwd"]()
-        if ev is not None:
-            ev[1].record()
-        s["bwd"]()
-        if ev is not None:
-            ev[2].record()
-
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    n_zero = int(sets[0]["zr"].sum().item())
-    n_nz = N - n_zero
-
-    # wall time of K steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-
-    # per-kernel durations over a second timed pass, events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
-    fwd_bytes = N * V * 2 + N * per_row_bytes_fwd()
-    bwd_bytes = N * V * 2 + n_nz * V * 2 + N * per_row_bytes_bwd()
-    step_bytes = fwd_bytes + bwd_bytes
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
-    bwd_gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
-    dom = ("grpo_bwd", bwd_gbs, bwd_ms, bwd_bytes) if bwd_ms >= fwd_ms else \
-          ("grpo_fwd", fwd_gbs, fwd_ms, fwd_bytes)
-
-    res = {
-        "metric": "GRPO logits fwd+bwd GB/s & % HBM peak at B4 L512 V32000 bf16; rows/s",
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "token-level GRPO logits fwd+bwd, B=4 L=512 V=32000 bf16 "
-                        "(T=0.9, beta=0.04, eps 0.2/0.28, 2 of 4 advantages 0, ref = policy, "
-                        "token-mean dloss, lengths U{256..512})",
-            "rows": N, "V": V, "zero_rows": n_zero, "nonzero_rows": n_nz,
-            "buffer_sets": args.sets, "accumulate": "fp32",
-        },
-        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "rows_per_s": round(N / (ms_step * 1e-3), 1),
-        "step_bytes": step_bytes,
-        "kernels": {
-            "grpo_fwd": {"ms": round(fwd_ms, 5), "bytes": fwd_bytes, "GB/s": round(fwd_gbs, 1)},
-            "grpo_bwd": {"ms": round(bwd_ms, 5), "bytes": bwd_bytes, "GB/s": round(bwd_gbs, 1)},
-        },
-        "roofline": {"kernel": dom[0], "bound": "hbm", "achieved": round(dom[1], 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom[1] / HBM_PEAK_GBS, 4),
-                     "traffic": None},
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, old)
+    if args.workload == "grpo-token":
+        res = run_grpo(args, torch, grl, synth, "token")
+    elif args.workload == "grpo-seq":
+        res = run_grpo(args, torch, grl, synth, "sequence")
+    elif args.workload == "rows":
+        res = run_rows(args, torch, grl, synth)
+    else:
+        res = run_fused(args, torch, grl, synth)
     print(json.dumps(res), flush=True)
 
 

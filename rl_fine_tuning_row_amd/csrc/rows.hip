@@ -282,14 +282,15 @@ struct Shape {
 
 // Default launch shapes (one workgroup per row), from a sweep on MI355X:
 // the forward, which ends in a workgroup reduction, prefers one wave per row
-// when there are few rows (a few thousand) and 512 lanes otherwise; the
+// when there are few (a few thousand) short (<= 128 KB) rows and 512 lanes
+// otherwise; the
 // backward, which streams a read and a write, prefers 1024 lanes per row.
 inline Shape pick_fwd_shape(int64_t rows, int64_t V, int es) {
   const LaunchOverride o = launch_override(0);
   if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
   const int64_t nvec = V * es / 16;
   if (nvec <= 512) return {64, 4};
-  if (rows <= 4096) return {64, 4};
+  if (rows <= 4096 && nvec <= 8192) return {64, 4};  // few, short rows
   return {512, 2};
 }
 
