@@ -226,7 +226,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   g2.N = int32_t(H);
   g2.K = int32_t(V);
   const int64_t per = (V + w.splits - 1) / w.splits;
-  g2.k_per_split = int32_t(((per + 31) / 32) * 32);
+  g2.k_per_split = int32_t(((per + 63) / 64) * 64);
   g2.split_stride = R * H;
   g2.C = w.splits > 1 ? z : grad_hidden;
   g2.ldc = H;
@@ -249,7 +249,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   g3.M = int32_t(V);
   g3.N = int32_t(H);
   g3.K = int32_t(R);
-  g3.k_per_split = int32_t(((R + 31) / 32) * 32);
+  g3.k_per_split = int32_t(((R + 63) / 64) * 64);
   if (gemm_bf16(false, false, GEMM_ACCUM, g3, 1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
   return GRPO_OK;
 }

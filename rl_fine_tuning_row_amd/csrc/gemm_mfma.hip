@@ -12,70 +12,171 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LROW = BK + 8;  // LDS row pitch in bf16 (80 bytes: 16-byte pad)
 constexpr int NTHREADS = 256;
 
-// Stage one operand tile (ROWS x BK, rows = M or N index) into registers.
-// K-contiguous: lane t loads chunks t and t + 256 (row = c / 4, 8 k each).
-// MN-contiguous: lane t loads K-rows 2q, 2q+1 (q = t % 4) of the 8 x 8 block
-// t / 4 (4 K-blocks x 16 row-blocks).
-template <bool KC>
-__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, int64_t ld, int extent,
-                                           int r0, int k0, int kend, v4u (&v)[2]) {
-  const int t = threadIdx.x;
-  if constexpr (KC) {
+// Tile configuration: BM x BN block tile, BK deep K step, 4 waves in a 2 x 2
+// grid, each wave (BM/2) x (BN/2) = TM x TN tiles of 32 x 32.
+template <int BM_, int BN_, int BK_, int WPE_ = 1>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WPE = WPE_;  // waves per SIMD the register budget must allow
+  static constexpr int LROW = BK + 8;  // LDS row pitch in bf16 (16-byte pad)
+  static constexpr int TM = BM / 64, TN = BN / 64;
+};
+
+// Staging of one ROWS x BK operand tile (rows = M or N index), in registers.
+//  K-contiguous: CPT = ROWS*BK/8/256 16-byte chunks per lane, chunk
+//    c = lane + 256 i covers row c / (BK/8), k-offset 8 (c % (BK/8)).
+//  MN-contiguous: the tile is (BK/8) x (ROWS/8) blocks of 8 x 8; TPB lanes
+//    share a block, each loading KPT = 8 / TPB consecutive K-rows of it.
+//    Successive blocks step along K first, so the lanes of a wave write
+//    their transposed rows side by side in LDS (no bank conflicts).
+template <int ROWS, int BK, bool KC>
+struct Stage {
+  static constexpr int CPT = ROWS * BK / 8 / NTHREADS;
+  static constexpr int BLOCKS = (BK / 8) * (ROWS / 8);
+  static constexpr int TPB = NTHREADS / BLOCKS;
+  static constexpr int KPT = 8 / (TPB > 0 ? TPB : 1);
+  static constexpr int NREG = KC ? CPT : KPT;
+  static_assert(KC ? (CPT >= 1) : (TPB >= 1 && TPB <= 8 && 8 % TPB == 0), "bad tile");
+
+  __device__ __forceinline__ static void load(const uint16_t* __restrict__ P, int64_t ld,
+                                              int extent, int r0, int k0, int kend,
+                                              v4u (&v)[NREG]) {
+    const int t = threadIdx.x;
+    if constexpr (KC) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + NTHREADS * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      const bool ok = (r0 + row < extent) && (k0 + kc < kend);
-      v[i] = ok ? *reinterpret_cast<const v4u*>(P + int64_t(r0 + row) * ld + k0 + kc)
-                : v4u{0u, 0u, 0u, 0u};
-    }
-  } else {
-    const int b = t >> 2, q = t & 3;
-    const int kb = b >> 4, rb = b & 15;
-    const bool col_ok = r0 + rb * 8 < extent;
+      for (int i = 0; i < CPT; ++i) {
+        const int c = t + NTHREADS * i;
+        const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        const bool ok = (r0 + row < extent) && (k0 + kc < kend);
+        v[i] = ok ? *reinterpret_cast<const v4u*>(P + int64_t(r0 + row) * ld + k0 + kc)
+                  : v4u{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const int b = t / TPB, q = t % TPB;
+      const int kb = b % (BK / 8), rb = b / (BK / 8);
+      const bool col_ok = r0 + rb * 8 < extent;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k = k0 + kb * 8 + 2 * q + i;
-      const bool ok = col_ok && (k < kend);
-      v[i] = ok ? *reinterpret_cast<const v4u*>(P + int64_t(k) * ld + r0 + rb * 8)
-                : v4u{0u, 0u, 0u, 0u};
+      for (int i = 0; i < KPT; ++i) {
+        const int k = k0 + kb * 8 + q * KPT + i;
+        const bool ok = col_ok && (k < kend);
+        v[i] = ok ? *reinterpret_cast<const v4u*>(P + int64_t(k) * ld + r0 + rb * 8)
+                  : v4u{0u, 0u, 0u, 0u};
+      }
     }
   }
-}
 
-// Write staged registers to an LDS tile laid out [row][k] with pitch LROW.
-template <bool KC>
-__device__ __forceinline__ void stage_store(uint16_t* __restrict__ lds, const v4u (&v)[2]) {
-  const int t = threadIdx.x;
-  if constexpr (KC) {
+  // Interior tiles (every chunk inside the operand): plain loads.
+  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
+                                                       int r0, int k0, v4u (&v)[NREG]) {
+    const int t = threadIdx.x;
+    if constexpr (KC) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + NTHREADS * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      *reinterpret_cast<v4u*>(lds + row * LROW + kc) = v[i];
-    }
-  } else {
-    const int b = t >> 2, q = t & 3;
-    const int kb = b >> 4, rb = b & 15;
-    uint32_t* base = reinterpret_cast<uint32_t*>(lds + (rb * 8) * LROW + kb * 8 + 2 * q);
-    const uint32_t x[4] = {v[0].x, v[0].y, v[0].z, v[0].w};  // K-row 2q, 8 rows' values
-    const uint32_t y[4] = {v[1].x, v[1].y, v[1].z, v[1].w};  // K-row 2q + 1
+      for (int i = 0; i < CPT; ++i) {
+        const int c = t + NTHREADS * i;
+        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(r0 + c / (BK / 8)) * ld + k0 +
+                                             (c % (BK / 8)) * 8);
+      }
+    } else {
+      const int b = t / TPB, q = t % TPB;
+      const int kb = b % (BK / 8), rb = b / (BK / 8);
+      const uint16_t* base = P + int64_t(k0 + kb * 8 + q * KPT) * ld + r0 + rb * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // element 2j (low halves) and 2j + 1 (high halves) of both K-rows
-      base[(2 * j) * (LROW / 2)] = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
-      base[(2 * j + 1) * (LROW / 2)] = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
+      for (int i = 0; i < KPT; ++i) v[i] = *reinterpret_cast<const v4u*>(base + int64_t(i) * ld);
     }
   }
-}
 
-template <bool A_KC, bool B_KC, int MODE>
-__global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmArgs g) {
+  // Branch-free variant for the pipelined kernel: every lane loads from a
+  // clamped, always-valid address; bit i of `ok` says whether chunk i lies
+  // inside the operand (store_masked zeroes the others).  Keeping the
+  // select out of the load lets the loads stay in flight across the MFMAs.
+  // Requires extent >= 1 (>= 8 when MN-contiguous) and kend >= 8.
+  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
+                                                      int extent, int r0, int k0, int kend,
+                                                      v4u (&v)[NREG], uint32_t& ok) {
+    const int t = threadIdx.x;
+    ok = 0u;
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = t + NTHREADS * i;
+        const int row = r0 + c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
+        ok |= uint32_t((row < extent) && (k < kend)) << i;
+        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(row, extent - 1)) * ld +
+                                             min(k, kend - 8));
+      }
+    } else {
+      const int b = t / TPB, q = t % TPB;
+      const int kb = b % (BK / 8), rb = b / (BK / 8);
+      const int col = r0 + rb * 8;
+      const bool col_ok = col < extent;
+      const int colc = min(col, extent - 8);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int k = k0 + kb * 8 + q * KPT + i;
+        ok |= uint32_t(col_ok && (k < kend)) << i;
+        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(k, kend - 1)) * ld + colc);
+      }
+    }
+  }
+
+  template <int LROW>
+  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
+                                                      uint32_t ok) {
+    const v4u zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) v[i] = ((ok >> i) & 1u) ? v[i] : zero;
+    store<LROW>(lds, v);
+  }
+
+  // write to an LDS tile laid out [row][k] with pitch LROW
+  template <int LROW>
+  __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
+    const int t = threadIdx.x;
+    if constexpr (KC) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = t + NTHREADS * i;
+        const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        *reinterpret_cast<v4u*>(lds + row * LROW + kc) = v[i];
+      }
+    } else {
+      // transpose: element e of the 8 rows' values of K-row i goes to LDS
+      // row (rb*8 + e), column kb*8 + q*KPT + i; pairs of K-rows share one
+      // 32-bit word (one v_perm_b32 each)
+      const int b = t / TPB, q = t % TPB;
+      const int kb = b % (BK / 8), rb = b / (BK / 8);
+      uint16_t* base = lds + (rb * 8) * LROW + kb * 8 + q * KPT;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[KPT / 2];
+#pragma unroll
+        for (int i = 0; i < KPT / 2; ++i) {
+          const uint32_t lo = v[2 * i][e >> 1], hi = v[2 * i + 1][e >> 1];
+          w[i] = __builtin_amdgcn_perm(hi, lo, sel);
+        }
+        uint16_t* dst = base + e * LROW;
+        if constexpr (KPT == 2) {
+          *reinterpret_cast<uint32_t*>(dst) = w[0];
+        } else if constexpr (KPT == 4) {
+          *reinterpret_cast<v2u*>(dst) = v2u{w[0], w[1]};
+        } else {
+          *reinterpret_cast<v4u*>(dst) = v4u{w[0], w[1], w[2], w[3]};
+        }
+      }
+    }
+  }
+};
+
+template <class C, bool A_KC, bool B_KC, int MODE>
+__global__ __launch_bounds__(NTHREADS, C::WPE) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LROW = C::LROW, TM = C::TM, TN = C::TN;
+  using SA = Stage<BM, BK, A_KC>;
+  using SB = Stage<BN, BK, B_KC>;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LROW];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LROW];
 
@@ -97,65 +198,66 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
-  v4u ra[2], rb[2];
-  stage_load<A_KC>(g.A, g.lda, g.M, m0, kbeg, kend, ra);
-  stage_load<B_KC>(g.B, g.ldb, g.N, n0, kbeg, kend, rb);
-  stage_store<A_KC>(As[0], ra);
-  stage_store<B_KC>(Bs[0], rb);
+  v4u ra[SA::NREG], rb[SB::NREG];
+  SA::load(g.A, g.lda, g.M, m0, kbeg, kend, ra);
+  SB::load(g.B, g.ldb, g.N, n0, kbeg, kend, rb);
+  SA::template store<LROW>(As[0], ra);
+  SB::template store<LROW>(Bs[0], rb);
   __syncthreads();
 
   int buf = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     const bool more = k0 + BK < kend;
     if (more) {
-      stage_load<A_KC>(g.A, g.lda, g.M, m0, k0 + BK, kend, ra);
-      stage_load<B_KC>(g.B, g.ldb, g.N, n0, k0 + BK, kend, rb);
+      SA::load(g.A, g.lda, g.M, m0, k0 + BK, kend, ra);
+      SB::load(g.B, g.ldb, g.N, n0, k0 + BK, kend, rb);
     }
-    const uint16_t* a_l = As[buf] + (wm * 64 + (lane & 31)) * LROW + 8 * (lane >> 5);
-    const uint16_t* b_l = Bs[buf] + (wn * 64 + (lane & 31)) * LROW + 8 * (lane >> 5);
+    const uint16_t* a_l = As[buf] + (wm * (BM / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
+    const uint16_t* b_l = Bs[buf] + (wn * (BN / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < TM; ++i)
         fa[i] = *reinterpret_cast<const bf16x8*>(a_l + i * 32 * LROW + s * 16);
-        fb[i] = *reinterpret_cast<const bf16x8*>(b_l + i * 32 * LROW + s * 16);
-      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int jj = 0; jj < TN; ++jj)
+        fb[jj] = *reinterpret_cast<const bf16x8*>(b_l + jj * 32 * LROW + s * 16);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
     }
     if (more) {
-      stage_store<A_KC>(As[buf ^ 1], ra);
-      stage_store<B_KC>(Bs[buf ^ 1], rb);
+      SA::template store<LROW>(As[buf ^ 1], ra);
+      SB::template store<LROW>(Bs[buf ^ 1], rb);
     }
     __syncthreads();
     buf ^= 1;
   }
 
-  float* C = g.C + int64_t(z) * g.split_stride;
+  float* Cp = g.C + int64_t(z) * g.split_stride;
   const int nl = lane & 31, mg = 4 * (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int n = n0 + wn * 64 + jj * 32 + nl;
+    for (int jj = 0; jj < TN; ++jj) {
+      const int n = n0 + wn * (BN / 2) + jj * 32 + nl;
       if (n >= g.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + mg + (r & 3);
+        const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + mg + (r & 3);
         if (m < g.M) {
-          float* p = C + int64_t(m) * g.ldc + n;
+          float* p = Cp + int64_t(m) * g.ldc + n;
           if constexpr (MODE == GEMM_ACCUM) *p += acc[i][jj][r];
           else *p = acc[i][jj][r];
         }
@@ -164,28 +266,250 @@ __global__ __launch_bounds__(NTHREADS) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <bool A_KC, bool B_KC>
-hipError_t launch(int mode, const GemmArgs& g, int splits, hipStream_t s) {
+// Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
+// so the wave itself must hide every latency).  Per K step (4 sub-steps of
+// 16): the next tile's global loads are issued at sub-step 0; each sub-step
+// reads the next sub-step's fragments from LDS into a second register set
+// while its 16 MFMAs run; the staged next tile is written to the other LDS
+// buffer during sub-step 2; one barrier ends the step.  The body has no
+// branches, and sched_group_barrier interleaves the memory instructions with
+// the MFMAs.
+// K loop of the pipelined kernel; EDGE selects masked loads (tiles that
+// overhang M, N or the K range) over plain ones.  Body is branch-free.
+template <class C, bool A_KC, bool B_KC, bool EDGE>
+__device__ __forceinline__ void pipe_mainloop(const GemmArgs& g, int m0, int n0, int kbeg,
+                                              int kend, uint16_t (*As)[C::BM * C::LROW],
+                                              uint16_t (*Bs)[C::BN * C::LROW],
+                                              f32x16 (&acc)[C::TM][C::TN]) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LROW = C::LROW, TM = C::TM, TN = C::TN;
+  constexpr int NS = BK / 16;
+  using SA = Stage<BM, BK, A_KC>;
+  using SB = Stage<BN, BK, B_KC>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  v4u ra[SA::NREG], rb[SB::NREG];
+  uint32_t oka = ~0u, okb = ~0u;
+  auto load = [&](int k) {
+    if constexpr (EDGE) {
+      SA::load_clamped(g.A, g.lda, g.M, m0, k, kend, ra, oka);
+      SB::load_clamped(g.B, g.ldb, g.N, n0, k, kend, rb, okb);
+    } else {
+      SA::load_interior(g.A, g.lda, m0, k, ra);
+      SB::load_interior(g.B, g.ldb, n0, k, rb);
+    }
+  };
+  auto store = [&](int b) {
+    if constexpr (EDGE) {
+      SA::template store_masked<LROW>(As[b], ra, oka);
+      SB::template store_masked<LROW>(Bs[b], rb, okb);
+    } else {
+      SA::template store<LROW>(As[b], ra);
+      SB::template store<LROW>(Bs[b], rb);
+    }
+  };
+  load(kbeg);
+  store(0);
+  __syncthreads();
+
+  const int a_off = (wm * (BM / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
+  const int b_off = (wn * (BN / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
+  bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(As[0] + a_off + i * 32 * LROW);
+#pragma unroll
+  for (int jj = 0; jj < TN; ++jj) fb[0][jj] = *reinterpret_cast<const bf16x8*>(Bs[0] + b_off + jj * 32 * LROW);
+
+  const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
+  int buf = 0;
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    // next tile (the last step reloads its own tile; that copy is never read)
+    load(min(k0 + BK, last));
+    const uint16_t* a_l = As[buf] + a_off;
+    const uint16_t* b_l = Bs[buf] + b_off;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s + 1 < NS) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[nxt][i] = *reinterpret_cast<const bf16x8*>(a_l + i * 32 * LROW + (s + 1) * 16);
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          fb[nxt][jj] = *reinterpret_cast<const bf16x8*>(b_l + jj * 32 * LROW + (s + 1) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][jj],
+                                                              acc[i][jj], 0, 0, 0);
+      if (s == 2) store(buf ^ 1);
+      // interleave the memory instructions with the MFMAs
+      if (s == 0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else if (s == 1) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else if (s == 2) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);   // DS write
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+    }
+    __syncthreads();
+    buf ^= 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(As[buf] + a_off + i * 32 * LROW);
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) fb[0][jj] = *reinterpret_cast<const bf16x8*>(Bs[buf] + b_off + jj * 32 * LROW);
+  }
+}
+
+// Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
+// so the wave itself must hide every latency).  Per K step (4 sub-steps of
+// 16): the next tile's global loads are issued at sub-step 0; each sub-step
+// reads the next sub-step's fragments from LDS into a second register set
+// while its 16 MFMAs run; the staged next tile is written to the other LDS
+// buffer during sub-step 2; one barrier ends the step.  sched_group_barrier
+// interleaves the memory instructions with the MFMAs.
+template <class C, bool A_KC, bool B_KC, int MODE>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
+  static_assert(BK == 64 && TM == 4 && TN == 4, "pipelined kernel expects 256 x 256 x 64");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * C::LROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * C::LROW];
+
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int id = blockIdx.x;
+  const int q = tiles / 8, rr = tiles % 8;
+  const int xcd = id % 8, j = id / 8;
+  const int t = xcd * q + min(xcd, rr) + j;
+  const int tm = t % g.tiles_m, tn = t / g.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int z = blockIdx.y;
+  const int kbeg = z * g.k_per_split;
+  const int kend = min(g.K, kbeg + g.k_per_split);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+
+  if (kend > kbeg) {
+    const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && ((kend - kbeg) % BK == 0);
+    if (interior) pipe_mainloop<C, A_KC, B_KC, false>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    else pipe_mainloop<C, A_KC, B_KC, true>(g, m0, n0, kbeg, kend, As, Bs, acc);
+  }
+
+  float* Cp = g.C + int64_t(z) * g.split_stride;
+  const int nl = lane & 31, mg = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < TN; ++jj) {
+      const int n = n0 + wn * (BN / 2) + jj * 32 + nl;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + mg + (r & 3);
+        if (m < g.M) {
+          float* p = Cp + int64_t(m) * g.ldc + n;
+          if constexpr (MODE == GEMM_ACCUM) *p += acc[i][jj][r];
+          else *p = acc[i][jj][r];
+        }
+      }
+    }
+  }
+}
+
+template <class C, bool A_KC, bool B_KC>
+hipError_t launch_pipe(int mode, GemmArgs g, int splits, hipStream_t s) {
+  g.tiles_m = (g.M + C::BM - 1) / C::BM;
+  g.tiles_n = (g.N + C::BN - 1) / C::BN;
   const dim3 grid(unsigned(g.tiles_m * g.tiles_n), unsigned(splits));
   if (mode == GEMM_ACCUM)
-    hipLaunchKernelGGL((gemm_bf16_kernel<A_KC, B_KC, GEMM_ACCUM>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_ACCUM>), grid, dim3(NTHREADS), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<A_KC, B_KC, GEMM_STORE>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_STORE>), grid, dim3(NTHREADS), 0, s, g);
   return hipGetLastError();
+}
+
+template <class C, bool A_KC, bool B_KC>
+hipError_t launch(int mode, GemmArgs g, int splits, hipStream_t s) {
+  g.tiles_m = (g.M + C::BM - 1) / C::BM;
+  g.tiles_n = (g.N + C::BN - 1) / C::BN;
+  const dim3 grid(unsigned(g.tiles_m * g.tiles_n), unsigned(splits));
+  if (mode == GEMM_ACCUM)
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, A_KC, B_KC, GEMM_ACCUM>), grid, dim3(NTHREADS), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, A_KC, B_KC, GEMM_STORE>), grid, dim3(NTHREADS), 0, s, g);
+  return hipGetLastError();
+}
+
+using Small = Cfg<128, 128, 32>;
+using Mid = Cfg<256, 128, 32, 2>;   // two workgroups per CU
+using Large = Cfg<256, 256, 64>;    // pipelined, one workgroup per CU
+
+template <class C>
+hipError_t launch_cfg(bool a_kc, bool b_kc, int mode, const GemmArgs& g, int splits,
+                      hipStream_t s) {
+  if (a_kc && b_kc) return launch<C, true, true>(mode, g, splits, s);
+  if (a_kc) return launch<C, true, false>(mode, g, splits, s);
+  if (b_kc) return launch<C, false, true>(mode, g, splits, s);
+  return launch<C, false, false>(mode, g, splits, s);
+}
+
+hipError_t launch_large(bool a_kc, bool b_kc, int mode, const GemmArgs& g, int splits,
+                        hipStream_t s) {
+  if (a_kc && b_kc) return launch_pipe<Large, true, true>(mode, g, splits, s);
+  if (a_kc) return launch_pipe<Large, true, false>(mode, g, splits, s);
+  if (b_kc) return launch_pipe<Large, false, true>(mode, g, splits, s);
+  return launch_pipe<Large, false, false>(mode, g, splits, s);
 }
 
 }  // namespace
 
-hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g_in, int splits,
+hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g, int splits,
                      hipStream_t s) {
-  GemmArgs g = g_in;
-  g.tiles_m = (g.M + BM - 1) / BM;
-  g.tiles_n = (g.N + BN - 1) / BN;
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  if (a_kcontig && b_kcontig) return launch<true, true>(mode, g, splits, s);
-  if (a_kcontig) return launch<true, false>(mode, g, splits, s);
-  if (b_kcontig) return launch<false, true>(mode, g, splits, s);
-  return launch<false, false>(mode, g, splits, s);
+  // Tile choice from measurements on MI355X: with both operands K-contiguous
+  // (the logits product) the pipelined 256 x 256 tile; with a transposed
+  // operand the 256 x 128 tile at two workgroups per CU, which overlaps one
+  // workgroup's staging and barrier with the other's MFMAs; small problems
+  // the 128 x 128 tile.
+  const int64_t mid_tiles = int64_t((g.M + 255) / 256) * ((g.N + 127) / 128) * splits;
+  if (a_kcontig && b_kcontig) {
+    const int64_t large_tiles = int64_t((g.M + 255) / 256) * ((g.N + 255) / 256) * splits;
+    if (large_tiles >= 512) return launch_large(true, true, mode, g, splits, s);
+  } else if (mid_tiles >= 512) {
+    return launch_cfg<Mid>(a_kcontig, b_kcontig, mode, g, splits, s);
+  }
+  return launch_cfg<Small>(a_kcontig, b_kcontig, mode, g, splits, s);
 }
 
 }  // namespace grpo
@@ -220,8 +544,8 @@ extern "C" int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const vo
   g.M = int32_t(M);
   g.N = int32_t(N);
   g.K = int32_t(K);
-  g.k_per_split = int32_t(((K + 31) / 32) * 32);
-  if (g.k_per_split == 0) g.k_per_split = 32;
+  g.k_per_split = int32_t(((K + 63) / 64) * 64);
+  if (g.k_per_split == 0) g.k_per_split = 64;
   g.split_stride = 0;
   const hipError_t e = gemm_bf16(akc, bkc, accumulate ? GEMM_ACCUM : GEMM_STORE, g, 1,
                                  static_cast<hipStream_t>(stream));

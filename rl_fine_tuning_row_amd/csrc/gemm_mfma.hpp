@@ -9,9 +9,14 @@
 //   grad_hidden  = dz W   : A = dz [R, V]  K-contig, B = W [V, H] N-contig
 //   grad_weight += dz^T h : A = dz [R, V]  M-contig, B = h [R, H] N-contig
 //
-// Block tile 128 x 128 x 32, 256 lanes = 4 waves in a 2 x 2 grid, each wave
-// a 64 x 64 tile of 2 x 2 v_mfma_f32_32x32x16_bf16 (accumulators in
-// registers).  Tiles are staged global -> registers -> LDS, double buffered:
+// Three block tiles, all 256 lanes = 4 waves in a 2 x 2 grid:
+//  * 256 x 256 x 64, software-pipelined (each wave 128 x 128 = 4 x 4
+//    v_mfma_f32_32x32x16_bf16, 256 accumulators per lane in AGPRs, one wave
+//    per SIMD, 144 KB of LDS) for the K-contiguous logits product;
+//  * 256 x 128 x 32 at two workgroups per CU for products with a transposed
+//    operand;
+//  * 128 x 128 x 32 for small problems.
+// Tiles are staged global -> registers -> LDS, double buffered:
 // the next tile's global loads are in flight while the current one feeds
 // the MFMAs.  LDS rows are K-contiguous with a 16-byte pad, so each lane's
 // 8-element operand fragment is one conflict-free 128-bit LDS read.  A
@@ -38,7 +43,7 @@ struct GemmArgs {
   float* C;
   int64_t ldc;
   int32_t M, N, K;
-  int32_t k_per_split;     // multiple of 32; split z covers [z*kps, min(K, (z+1)*kps))
+  int32_t k_per_split;     // multiple of 64; split z covers [z*kps, min(K, (z+1)*kps))
   int64_t split_stride;    // elements between the split-K partial slabs of C
   int32_t tiles_m, tiles_n;
 };
