@@ -7,9 +7,11 @@ Default workload ``grpo-token`` (the headline): a step is one forward +
 backward of the token-level GRPO loss over the logits of B=4 sequences x
 L=512 tokens x V=32000 vocabulary entries (bf16, T=0.9, beta=0.04, eps
 0.2/0.28, half the advantages exactly 0, no reference model so the KL term
-vanishes, token-mean upstream gradient): grpo_logits_fwd writes loss, logp,
-lse, entropy, kl and is_clipped per token; grpo_logits_bwd writes dlogits,
-with the all-zero path on rows whose dlogp is 0.  S buffer sets (about 1 GB
+vanishes, token-mean upstream gradient), run as the single pass
+grpo_logits_fwd_bwd: loss, logp, lse, entropy, kl and is_clipped per token
+and dlogits (all-zero rows where dlogp is 0) from one read of the logits.
+The two-pass step (grpo_logits_fwd then grpo_logits_bwd) is timed too and
+reported under "two_pass".  S buffer sets (about 1 GB
 in total by default) rotate from step to step so a step does not find the
 previous step's logits in the 256 MB last-level cache.
 
@@ -147,12 +149,18 @@ def base_line(args, metric, value, unit, ms, config, dtype="bf16"):
 # per-row scalar bytes of the GRPO kernels
 FWD_ROW_BYTES = 8 + 4 + 5 * 4 + 1      # ids, old_logp in; loss, logp, lse, entropy, kl, is_clipped out
 BWD_ROW_BYTES = 8 + 4 + 4 + 4 + 4 + 1  # ids, old_logp, logp, lse, dloss in; zero_row out
+ONE_ROW_BYTES = 8 + 4 + 4 + 5 * 4 + 1 + 1  # ids, old_logp, dloss in; 5 fp32, is_clipped, zero_row out
 
 
 # ---------------------------------------------------------------------------
 # GRPO token / sequence level
 # ---------------------------------------------------------------------------
 def run_grpo(args, torch, grl, synth, level):
+    """Token level: the step is the single-pass grpo_logits_fwd_bwd (dloss of
+    a token-mean loss is known before the forward); the two-pass
+    grpo_logits_fwd + grpo_logits_bwd step is timed as well and reported under
+    "two_pass".  Sequence level (needs the per-sequence ratio before any
+    gradient): the two-pass step."""
     if level == "token":
         case = synth.grpo_token_case(with_ref=False, dloss="mean")
         name = "token"
@@ -168,7 +176,7 @@ def run_grpo(args, torch, grl, synth, level):
                                     dev(case.dloss))
     nsets = args.sets if level == "token" else 2
     kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
-              eps_high=case.eps_high, level=level)
+              eps_high=case.eps_high)
     sets = []
     for k in range(nsets):
         z = z0.clone() if k else z0
@@ -177,34 +185,59 @@ def run_grpo(args, torch, grl, synth, level):
         out["is_clipped"] = torch.empty(N, dtype=torch.uint8, device="cuda")
         dz = torch.empty((N, V), dtype=torch.bfloat16, device="cuda")
         zr = torch.empty(N, dtype=torch.uint8, device="cuda")
-        # arguments marshalled once; a step is two C calls
+        # arguments marshalled once; a step is one (single pass) or two C calls
         fwd, out = grl.grpo_logits_fwd(z, ids, old_t, adv, B, L, mask=mask, out=out,
-                                       prepare=True, **kw)
+                                       prepare=True, level=level, **kw)
         bwd, _, _ = grl.grpo_logits_bwd(z, ids, old_t, adv, B, L, out["logp"], out["lse"],
                                         dloss, mask=mask, seq_ratio=out.get("seq_ratio"),
-                                        dlogits=dz, zero_row=zr, prepare=True, **kw)
-        sets.append(dict(fwd=fwd, bwd=bwd, zr=zr))
-    steps = [(lambda s=s: (s["fwd"](), s["bwd"]())) for s in sets]
+                                        dlogits=dz, zero_row=zr, prepare=True, level=level, **kw)
+        one = None
+        if level == "token":
+            one, _, _, _ = grl.grpo_logits_fwd_bwd(z, ids, old_t, adv, B, L, dloss, mask=mask,
+                                                   out=out, dlogits=dz, zero_row=zr,
+                                                   prepare=True, **kw)
+        sets.append(dict(fwd=fwd, bwd=bwd, one=one, zr=zr))
+    two_steps = [(lambda s=s: (s["fwd"](), s["bwd"]())) for s in sets]
     for i in range(args.warmup):
-        steps[i % len(steps)]()
+        two_steps[i % len(two_steps)]()
+        if level == "token":
+            sets[i % len(sets)]["one"]()
     torch.cuda.synchronize()
     n_zero = int(sets[0]["zr"].sum().item())
     n_nz = N - n_zero
-    ms = timed(steps, args.steps, torch)
-    fwd_ms, bwd_ms = kernel_times([[s["fwd"], s["bwd"]] for s in sets], args.steps, torch)
     fwd_bytes = N * V * 2 + N * FWD_ROW_BYTES
     bwd_bytes = N * V * 2 + n_nz * V * 2 + N * BWD_ROW_BYTES
-    step_bytes = fwd_bytes + bwd_bytes
+    two_bytes = fwd_bytes + bwd_bytes
+    ms_two = timed(two_steps, args.steps, torch)
+    fwd_ms, bwd_ms = kernel_times([[s["fwd"], s["bwd"]] for s in sets], args.steps, torch)
+    two_pass = {
+        "ms_per_step": round(ms_two, 5), "step_bytes": two_bytes,
+        "GB/s": round(two_bytes / (ms_two * 1e-3) / 1e9, 1),
+        "rows_per_s": round(N / (ms_two * 1e-3), 1),
+        "kernels": {"grpo_fwd": {"ms": round(fwd_ms, 5), "bytes": fwd_bytes,
+                                 "GB/s": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1)},
+                    "grpo_bwd": {"ms": round(bwd_ms, 5), "bytes": bwd_bytes,
+                                 "GB/s": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1)}}}
+    if level == "token":
+        # single pass: logits read once, dlogits written once
+        one_bytes = 2 * N * V * 2 + N * ONE_ROW_BYTES
+        ms = timed([s["one"] for s in sets], args.steps, torch)
+        (one_ms,) = kernel_times([[s["one"]] for s in sets], args.steps, torch)
+        step_bytes = one_bytes
+        kern = {"grpo_fwd_bwd": (one_ms, one_bytes)}
+    else:
+        ms = ms_two
+        step_bytes = two_bytes
+        kern = {"grpo_fwd": (fwd_ms, fwd_bytes), "grpo_bwd": (bwd_ms, bwd_bytes)}
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    kern = {"grpo_fwd": (fwd_ms, fwd_bytes), "grpo_bwd": (bwd_ms, bwd_bytes)}
     dom = max(kern, key=lambda k: kern[k][0])
     dom_gbs = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e9
     wl = "grpo-token" if level == "token" else "grpo-seq"
     if level == "token":
         metric = "GRPO logits fwd+bwd GB/s & % HBM peak at B4 L512 V32000 bf16; rows/s"
-        desc = ("token-level GRPO logits fwd+bwd, B=4 L=512 V=32000 bf16 (T=0.9, beta=0.04, "
-                "eps 0.2/0.28, 2 of 4 advantages 0, ref = policy, token-mean dloss, "
-                "lengths U{256..512})")
+        desc = ("token-level GRPO logits fwd+bwd in one pass (grpo_logits_fwd_bwd), B=4 L=512 "
+                "V=32000 bf16 (T=0.9, beta=0.04, eps 0.2/0.28, 2 of 4 advantages 0, "
+                "ref = policy, token-mean dloss, lengths U{256..512})")
     else:
         metric = "GRPO sequence-level logits fwd+bwd GB/s at B8 L1024 V151936 bf16; rows/s"
         desc = ("sequence-level GRPO logits fwd+bwd, B=8 L=1024 V=151936 bf16 (T=1, beta=0, "
@@ -223,6 +256,8 @@ def run_grpo(args, torch, grl, synth, level):
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(dom, wl)},
     })
+    if level == "token":
+        res["two_pass"] = two_pass
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_grpo(case, old, level)
     return res

@@ -161,6 +161,33 @@ int grpo_logits_bwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t
                     int64_t ld_out, uint8_t* zero_row, void* stream);
 
 /* ------------------------------------------------------------------------
+ * grpo_logits_fwd_bwd -- forward and backward of the token-level loss in a
+ * single pass, for callers that know the per-token upstream weight dloss
+ * before the forward (a token-mean or sum reduction of the per-token loss;
+ * the chunked loss of [LIGER-TRL] items 3-4 computes gradients during the
+ * forward in the same way).  Computes exactly what grpo_logits_fwd followed
+ * by grpo_logits_bwd compute (same definitions, same early all-zero rows),
+ * but each row is read once into registers and dlogits written from them.
+ * Rows longer than 128 KB, or not 16-byte aligned, take the two-pass path
+ * internally (then dlogits may not alias logits).  level must be
+ * GRPO_TOKEN (GRPO_ERR_PARAM otherwise).
+ *
+ * Arguments as grpo_logits_fwd / grpo_logits_bwd: logits, ids, old_logp,
+ * ref_logp (nullable), adv, mask (unused at token level), p, dloss (in);
+ * loss, logp, lse (out, required); entropy, kl, is_clipped (out, nullable);
+ * dlogits [B*L, ld_out] of `dtype` (out; may alias logits if ld_out == ld
+ * and the row fits in registers); zero_row (out, nullable); err_count
+ * (nullable).
+ * ------------------------------------------------------------------------ */
+int grpo_logits_fwd_bwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,
+                        int64_t ld, const int64_t* ids, const float* old_logp,
+                        const float* ref_logp, const float* adv, const uint8_t* mask,
+                        const grpo_params* p, const float* dloss, float* loss, float* logp,
+                        float* lse, float* entropy, float* kl, uint8_t* is_clipped,
+                        void* dlogits, int64_t ld_out, uint8_t* zero_row, int32_t* err_count,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
  * entropy_from_logits -- per-row entropy of softmax(z / temperature).
  * Defines [AXOLOTL part 1: minus the row sum of exp(logp) * logp of the row
  * log-softmax; strided rows read in place].  temperature 1 is the plain op.

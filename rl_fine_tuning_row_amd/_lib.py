@@ -49,6 +49,9 @@ _SIGS = {
                         ctypes.POINTER(GrpoParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "grpo_logits_bwd": [_P, _I, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
                         ctypes.POINTER(GrpoParams), _P, _P, _P, _P, _P, _I64, _P, _P],
+    "grpo_logits_fwd_bwd": [_P, _I, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                            ctypes.POINTER(GrpoParams), _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P,
+                            _P, _P],
     "entropy_from_logits": [_P, _I, _I64, _I64, _I64, _F, _P, _P],
     "selective_log_softmax": [_P, _I, _I64, _I64, _I64, _P, _F, _P, _P, _P],
     "selective_log_softmax_bwd": [_P, _I, _I64, _I64, _I64, _P, _F, _P, _P, _P, _I64, _P],
@@ -234,6 +237,58 @@ def grpo_logits_bwd(logits, ids, old_logp, adv, B, L, logp, lse, dloss, *, ref_l
         return launch, dlogits, zr
     launch()
     return dlogits, zr
+
+
+def grpo_logits_fwd_bwd(logits, ids, old_logp, adv, B, L, dloss, *, ref_logp=None, mask=None,
+                        temperature=1.0, beta=0.0, eps_low=0.2, eps_high=0.2,
+                        force_dense=False, entropy=True, kl=True, is_clipped=True,
+                        dlogits=None, zero_row=True, err_count=None, out=None, stream=None,
+                        prepare=False):
+    """Single-pass token-level forward + backward.  Returns (outputs, dlogits,
+    zero_row); with ``prepare=True`` returns (launch, outputs, dlogits, zero_row)."""
+    rows, V, ld = _rows_view(logits)
+    if rows != B * L:
+        raise ValueError(f"logits has {rows} rows, expected B*L = {B * L}")
+    f32 = torch.float32
+    dev = logits.device
+    for t, dt, n, nm in ((ids, torch.int64, rows, "ids"), (old_logp, f32, rows, "old_logp"),
+                         (ref_logp, f32, rows, "ref_logp"), (adv, f32, B, "adv"),
+                         (mask, torch.uint8, rows, "mask"), (dloss, f32, rows, "dloss"),
+                         (err_count, torch.int32, 1, "err_count")):
+        _need(t, dt, n, nm)
+    o = dict(out or {})
+
+    def get(name, dtype, want=True):
+        if name in o:
+            return _need(o[name], dtype, rows, name)
+        if not want:
+            return None
+        o[name] = torch.empty(rows, dtype=dtype, device=dev)
+        return o[name]
+
+    outs = [get("loss", f32), get("logp", f32), get("lse", f32), get("entropy", f32, entropy),
+            get("kl", f32, kl), get("is_clipped", torch.uint8, is_clipped)]
+    if dlogits is None:
+        dlogits = torch.empty((rows, V), dtype=logits.dtype, device=dev)
+    r2, v2, ld_out = _rows_view(dlogits)
+    if (r2, v2) != (rows, V) or dlogits.dtype != logits.dtype:
+        raise ValueError("dlogits must be [rows, V] of the logits' dtype")
+    zr = None
+    if zero_row is True:
+        zr = torch.empty(rows, dtype=torch.uint8, device=dev)
+    elif zero_row is not False and zero_row is not None:
+        zr = _need(zero_row, torch.uint8, rows, "zero_row")
+    p = _params(temperature, beta, eps_low, eps_high, "token",
+                GRPO_FLAG_FORCE_DENSE if force_dense else 0)
+    cargs = (_ptr(logits), _dtype_code(logits), B, L, V, ld, _ptr(ids), _ptr(old_logp),
+             _ptr(ref_logp), _ptr(adv), _ptr(mask), ctypes.byref(p), _ptr(dloss),
+             *[_ptr(t) for t in outs], _ptr(dlogits), ld_out, _ptr(zr), _ptr(err_count),
+             _stream(stream))
+    launch = _launcher("grpo_logits_fwd_bwd", cargs, keep=(p,))
+    if prepare:
+        return launch, o, dlogits, zr
+    launch()
+    return o, dlogits, zr
 
 
 def entropy_from_logits(logits, temperature=1.0, out=None, stream=None):

@@ -13,6 +13,8 @@
 // without touching the logits.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "grpo_rows.h"
 #include "host_common.hpp"
 #include "row_core.hpp"
@@ -274,6 +276,166 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// single pass: forward and backward of the token-level loss in one read
+// ---------------------------------------------------------------------------
+// When the per-token upstream weight dloss is known before the forward (a
+// token-mean or sum reduction), one workgroup reads its row once into
+// registers (VPT 128-bit vectors per lane), computes the row statistics,
+// the per-token loss and dlogp from them, and writes dlogits from the same
+// registers: the logits are read once and dlogits written once.  Vectors past
+// the row end are filled with a large negative finite value, so they add
+// nothing to the max or the sums and are never stored.
+struct FusedArgs {
+  FwdArgs f;
+  void* dlogits;
+  int64_t ld_out;
+  const float* dloss;
+  uint8_t* zero_row;
+  int32_t force_dense;
+};
+
+// Opaque to the optimiser: the packed row stays the only copy in registers
+// and each pass unpacks it again (two VALU ops per pair) instead of the
+// compiler keeping every unpacked float alive across the passes.
+__device__ __forceinline__ void keep_packed(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+template <typename TIn> struct Fill;
+template <> struct Fill<uint16_t> { static constexpr uint32_t bits = 0xF149F149u; };  // bf16 ~ -1e30
+template <> struct Fill<float> { static constexpr uint32_t bits = 0xF149F2CAu; };     // -1e30f
+
+template <typename TIn, int WG, int VPT, bool NEED_T>
+__global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
+  constexpr int VE = Vec<TIn>::N;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const FwdArgs& f = a.f;
+  const TIn* __restrict__ row = static_cast<const TIn*>(f.logits) + r * f.ld;
+  const int V = f.V;
+  const int nvec = V / VE;
+  const float c = f.c;
+  const u32x4* __restrict__ rv = reinterpret_cast<const u32x4*>(row);
+  const u32x4 fill = {Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits};
+
+  u32x4 v[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * WG;
+    v[i] = idx < nvec ? load16<false>(rv + idx) : fill;
+  }
+  const int jt = nvec * VE + tid;  // the V % VE tail elements, one per lane
+  const bool has_tail = jt < V;
+  const float xt = has_tail ? load_elem(row + jt) : __uint_as_float(0xF149F2CAu);
+
+  // lane statistics over the registers: max first, then the sums
+  float m = xt;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    float x[VE];
+    Vec<TIn>::unpack(v[i], x);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) m = fmaxf(m, x[k]);
+  }
+  const float mc = m * c;
+  float s = 0.0f, t = 0.0f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    keep_packed(v[i]);
+    float x[VE];
+    Vec<TIn>::unpack(v[i], x);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) {
+      const float d = fmaf(x[k], c, -mc);
+      const float e = exp2_fast(d);
+      s += e;
+      if (NEED_T) t = fmaf(e, d, t);
+    }
+  }
+  {
+    const float d = fmaf(xt, c, -mc);
+    const float e = exp2_fast(d);
+    s += e;
+    if (NEED_T) t = fmaf(e, d, t);
+  }
+  Stat st;
+  st.m = m;
+  st.s = s;
+  st.t = NEED_T ? t : 0.0f;
+  st = block_reduce_stat<WG, NEED_T>(st, c);
+
+  // per-token epilogue, computed alike in every lane
+  const float logS = logf(st.s);
+  const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
+  const int64_t y = f.ids[r];
+  const bool valid = y >= 0 && y < V;
+  const float zy = valid ? load_elem(row + y) : __builtin_nanf("");
+  const float lse = st.m / f.T + logS;
+  const float logp = (zy - st.m) / f.T - logS;
+  float kl = 0.0f;
+  if (f.ref_logp != nullptr) {
+    const float d = f.ref_logp[r] - logp;
+    kl = expm1f(d) - d;
+  }
+  const float A = f.adv[r / f.L];
+  const Ppo q = ppo_terms(logp - f.old_logp[r], A, f.lo, f.hi);
+  const float w = a.dloss[r];
+  float klg = 0.0f;
+  if (f.ref_logp != nullptr && f.beta != 0.0f) klg = -f.beta * expm1f(f.ref_logp[r] - logp);
+  const float g = uniform(((q.clipped ? 0.0f : -q.ratio * A) + klg) * w);
+  const bool zero = (g == 0.0f);
+  if (tid == 0) {
+    if (!valid && f.err_count != nullptr) atomicAdd(f.err_count, 1);
+    f.logp[r] = logp;
+    f.lse[r] = lse;
+    if (f.entropy != nullptr) f.entropy[r] = H;
+    if (f.kl != nullptr) f.kl[r] = kl;
+    f.loss[r] = q.pg + (f.beta != 0.0f ? f.beta * kl : 0.0f);
+    if (f.is_clipped != nullptr) f.is_clipped[r] = q.clipped ? 1 : 0;
+    if (a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
+  }
+
+  TIn* __restrict__ out = static_cast<TIn*>(a.dlogits) + r * a.ld_out;
+  u32x4* __restrict__ ov = reinterpret_cast<u32x4*>(out);
+  if (!valid) {
+    for (int j = tid; j < V; j += WG) store_elem(out + j, __builtin_nanf(""));
+    return;
+  }
+  if (zero && !a.force_dense) {
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int idx = tid + i * WG;
+      if (idx < nvec) store16(ov + idx, z4);
+    }
+    if (has_tail) store_elem(out + jt, 0.0f);
+    return;
+  }
+  const float coef = g / f.T;
+  const float lse2 = lse * kLog2e;
+  const int yi = int(y);
+  const int vy = yi / VE, ky = yi % VE;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * WG;
+    keep_packed(v[i]);
+    float x[VE];
+    Vec<TIn>::unpack(v[i], x);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
+    if (idx == vy) {
+#pragma unroll
+      for (int k = 0; k < VE; ++k)
+        if (k == ky) x[k] += coef;
+    }
+    if (idx < nvec) store16(ov + idx, Vec<TIn>::pack(x));
+  }
+  if (has_tail) {
+    float d = -coef * exp2_fast(fmaf(xt, c, -lse2));
+    if (jt == yi) d += coef;
+    store_elem(out + jt, d);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launch shape dispatch
 // ---------------------------------------------------------------------------
 struct Shape {
@@ -393,6 +555,62 @@ int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
                                   : launch_bwd_t<uint16_t, uint16_t, false>(a, rows, sh, s);
   else e = vec ? launch_bwd_t<float, float, true>(a, rows, sh, s)
                : launch_bwd_t<float, float, false>(a, rows, sh, s);
+  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+// Single-pass launch: the smallest workgroup (256 or 512 lanes) whose lanes
+// can hold the row in 16 vectors each; rows longer than 128 KB do not fit.
+// Returns false (nothing launched) when the row does not fit or the rows are
+// not 16-byte aligned.
+template <typename TIn, bool NEED_T>
+hipError_t launch_fused_t(const FusedArgs& a, int64_t rows, int wg, int vpt, hipStream_t s) {
+#define X(W, P)                                                                        \
+  if (wg == W && vpt == P) {                                                            \
+    hipLaunchKernelGGL((row_fused_kernel<TIn, W, P, NEED_T>), dim3(unsigned(rows)),     \
+                       dim3(W), 0, s, a);                                               \
+    return hipGetLastError();                                                           \
+  }
+  X(256, 8)
+  X(256, 16)
+  X(512, 8)
+  X(512, 16)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
+bool fused_shape(int64_t V, int es, int& wg, int& vpt) {
+  const LaunchOverride o = parse_launch(std::getenv("GRPO_ROWS_FUSED_LAUNCH"));
+  const int64_t nvec = V * es / 16;
+  if (o.wg > 0 && o.unroll > 0) {
+    wg = o.wg;
+    vpt = o.unroll;
+    return int64_t(wg) * vpt >= nvec;
+  }
+  for (int w : {256, 512}) {
+    if (int64_t(w) * 16 >= nvec) {
+      wg = w;
+      vpt = int64_t(w) * 8 >= nvec ? 8 : 16;
+      return true;
+    }
+  }
+  return false;
+}
+
+int launch_fused(const FusedArgs& a, int dtype, int64_t rows, bool need_t, bool& launched,
+                 hipStream_t s) {
+  const int es = elem_size(dtype);
+  launched = false;
+  int wg = 0, vpt = 0;
+  if (!fused_shape(a.f.V, es, wg, vpt)) return GRPO_OK;
+  if (!rows_vec_ok(a.f.logits, a.f.ld, es) || !rows_vec_ok(a.dlogits, a.ld_out, es)) return GRPO_OK;
+  hipError_t e;
+  if (dtype == GRPO_BF16)
+    e = need_t ? launch_fused_t<uint16_t, true>(a, rows, wg, vpt, s)
+               : launch_fused_t<uint16_t, false>(a, rows, wg, vpt, s);
+  else
+    e = need_t ? launch_fused_t<float, true>(a, rows, wg, vpt, s)
+               : launch_fused_t<float, false>(a, rows, wg, vpt, s);
+  launched = (e == hipSuccess);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
@@ -536,6 +754,89 @@ extern "C" int grpo_logits_bwd(const void* logits, int dtype, int64_t B, int64_t
   a.force_dense = (p->flags & GRPO_FLAG_FORCE_DENSE) ? 1 : 0;
   a.zero_row = zero_row;
   return launch_bwd(a, dtype, rows, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grpo_logits_fwd_bwd(const void* logits, int dtype, int64_t B, int64_t L,
+                                   int64_t V, int64_t ld, const int64_t* ids,
+                                   const float* old_logp, const float* ref_logp,
+                                   const float* adv, const uint8_t* mask, const grpo_params* p,
+                                   const float* dloss, float* loss, float* logp, float* lse,
+                                   float* entropy, float* kl, uint8_t* is_clipped,
+                                   void* dlogits, int64_t ld_out, uint8_t* zero_row,
+                                   int32_t* err_count, void* stream) {
+  int st = check_grpo_common(logits, dtype, B, L, V, ld, ids, old_logp, ref_logp, adv, mask, p);
+  if (st != GRPO_OK) return st;
+  if (p->level != GRPO_TOKEN) return GRPO_ERR_PARAM;
+  const int64_t rows = B * L;
+  if (ld_out < V) return GRPO_ERR_STRIDE;
+  if (dlogits == logits && ld_out != ld) return GRPO_ERR_STRIDE;
+  if (rows > 0 && (dloss == nullptr || loss == nullptr || logp == nullptr || lse == nullptr ||
+                   dlogits == nullptr))
+    return GRPO_ERR_NULL;
+  for (const void* q : {(const void*)dloss, (const void*)loss, (const void*)logp,
+                        (const void*)lse, (const void*)entropy, (const void*)kl,
+                        (const void*)err_count})
+    if (!aligned(q, 4)) return GRPO_ERR_ALIGN;
+  if (!aligned(dlogits, elem_size(dtype))) return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  FusedArgs a{};
+  a.f.logits = logits;
+  a.f.ld = ld;
+  a.f.V = int32_t(V);
+  a.f.L = int32_t(L);
+  a.f.ids = ids;
+  a.f.old_logp = old_logp;
+  a.f.ref_logp = ref_logp;
+  a.f.adv = adv;
+  fill_loss_params(p, a.f.T, a.f.c, a.f.lo, a.f.hi);
+  a.f.beta = p->beta;
+  a.f.mode = FWD_GRPO;
+  a.f.level = GRPO_TOKEN;
+  a.f.loss = loss;
+  a.f.logp = logp;
+  a.f.lse = lse;
+  a.f.entropy = entropy;
+  a.f.kl = kl;
+  a.f.is_clipped = is_clipped;
+  a.f.err_count = err_count;
+  a.dlogits = dlogits;
+  a.ld_out = ld_out;
+  a.dloss = dloss;
+  a.zero_row = zero_row;
+  a.force_dense = (p->flags & GRPO_FLAG_FORCE_DENSE) ? 1 : 0;
+  bool launched = false;
+  st = launch_fused(a, dtype, rows, entropy != nullptr, launched, s);
+  if (st != GRPO_OK || launched) return st;
+  // rows too long for registers (or not 16-byte aligned): forward then backward
+  if (dlogits == logits) return GRPO_ERR_STRIDE;  // the backward would read overwritten rows
+  st = launch_fwd(a.f, dtype, rows, entropy != nullptr, s);
+  if (st != GRPO_OK) return st;
+  BwdArgs b{};
+  b.logits = logits;
+  b.ld = ld;
+  b.dlogits = dlogits;
+  b.ld_out = ld_out;
+  b.V = int32_t(V);
+  b.L = int32_t(L);
+  b.ids = ids;
+  b.old_logp = old_logp;
+  b.ref_logp = ref_logp;
+  b.adv = adv;
+  b.mask = mask;
+  b.logp = logp;
+  b.lse = lse;
+  b.dloss = dloss;
+  b.T = a.f.T;
+  b.c = a.f.c;
+  b.beta = a.f.beta;
+  b.lo = a.f.lo;
+  b.hi = a.f.hi;
+  b.mode = BWD_GRPO;
+  b.level = GRPO_TOKEN;
+  b.force_dense = a.force_dense;
+  b.zero_row = zero_row;
+  return launch_bwd(b, dtype, rows, s);
 }
 
 extern "C" int entropy_from_logits(const void* logits, int dtype, int64_t rows, int64_t V,
