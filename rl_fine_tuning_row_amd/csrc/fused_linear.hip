@@ -34,11 +34,12 @@ struct WsLayout {
   int splits;
 };
 
-// K-splits of grad_hidden = dz W so that (tiles x splits) fills the chip.
+// K-splits of grad_hidden = dz W so that the 256 x 256 tiles times the
+// splits give at least two workgroups per CU.
 int pick_splits(int64_t R, int64_t H) {
-  const int64_t tiles = ((R + 127) / 128) * ((H + 127) / 128);
+  const int64_t tiles = ((R + 255) / 256) * ((H + 255) / 256);
   int s = 1;
-  while (tiles * s < 1024 && s < 16) s *= 2;
+  while (tiles * s < 512 && s < 16) s *= 2;
   return s;
 }
 

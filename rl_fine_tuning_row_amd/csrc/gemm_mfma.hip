@@ -10,6 +10,7 @@ namespace grpo {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
@@ -172,6 +173,114 @@ struct Stage {
   }
 };
 
+// Operand handling of the pipelined kernel, one ROWS x BK tile per K step.
+//  K-contiguous: LDS [row][k], pitch BK + 8; a fragment is one 128-bit read.
+//  MN-contiguous: LDS [k][row], pitch ROWS + 32, filled by plain 16-byte
+//    copies (no register transpose); a fragment is two ds_read_b64_tr_b16.
+//    That instruction, within each 16-lane group, gives lane i as element j
+//    the 16-bit value at (address of lane 4 j + i / 4) + i % 4 (checked on
+//    MI355X).  So if lane q of the group points at K-row kb + q / 4, columns
+//    c + 4 (q % 4) .. +3, lane i receives rows kb .. kb+3 of column c + i:
+//    the K-run the MFMA fragment wants.  The 32-element pad puts the four
+//    K-rows one read touches on disjoint bank quarters.
+template <int ROWS, int BK, bool KC>
+struct PipeOp;
+
+template <int ROWS, int BK>
+struct PipeOp<ROWS, BK, true> {
+  using S = Stage<ROWS, BK, true>;
+  static constexpr int PITCH = BK + 8;
+  static constexpr int ELEMS = ROWS * PITCH;
+  static constexpr int NREG = S::NREG;
+  static constexpr int READS = 1;  // LDS instructions per fragment
+  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
+                                                       int r0, int k0, v4u (&v)[NREG]) {
+    S::load_interior(P, ld, r0, k0, v);
+  }
+  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
+                                                      int extent, int r0, int k0, int kend,
+                                                      v4u (&v)[NREG], uint32_t& ok) {
+    S::load_clamped(P, ld, extent, r0, k0, kend, v, ok);
+  }
+  __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
+    S::template store<PITCH>(lds, v);
+  }
+  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
+                                                      uint32_t ok) {
+    S::template store_masked<PITCH>(lds, v, ok);
+  }
+  // lane's fragment base for the wave's half `h` of the tile's rows
+  __device__ __forceinline__ static int lane_offset(int h, int lane) {
+    return (h * (ROWS / 2) + (lane & 31)) * PITCH + 8 * (lane >> 5);
+  }
+  // fragment of 32-row block i, K sub-step s (16 deep)
+  __device__ __forceinline__ static bf16x8 frag(const uint16_t* tile, int off, int i, int s) {
+    return *reinterpret_cast<const bf16x8*>(tile + off + i * 32 * PITCH + s * 16);
+  }
+};
+
+template <int ROWS, int BK>
+struct PipeOp<ROWS, BK, false> {
+  static constexpr int PITCH = ROWS + 32;
+  static constexpr int ELEMS = BK * PITCH;
+  static constexpr int RC = ROWS / 8;  // 16-byte chunks per K-row
+  static constexpr int NREG = ROWS * BK / 8 / NTHREADS;
+  static constexpr int READS = 2;
+  static_assert(NREG >= 1 && NREG <= 32, "bad tile");
+  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
+                                                       int r0, int k0, v4u (&v)[NREG]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const int c = t + NTHREADS * i;
+      v[i] = *reinterpret_cast<const v4u*>(P + int64_t(k0 + c / RC) * ld + r0 + (c % RC) * 8);
+    }
+  }
+  // requires extent % 8 == 0, extent >= 8 and kend >= 1
+  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
+                                                      int extent, int r0, int k0, int kend,
+                                                      v4u (&v)[NREG], uint32_t& ok) {
+    const int t = threadIdx.x;
+    ok = 0u;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const int c = t + NTHREADS * i;
+      const int k = k0 + c / RC, row = r0 + (c % RC) * 8;
+      ok |= uint32_t((row < extent) && (k < kend)) << i;
+      v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(k, kend - 1)) * ld +
+                                           min(row, extent - 8));
+    }
+  }
+  __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      const int c = t + NTHREADS * i;
+      *reinterpret_cast<v4u*>(lds + (c / RC) * PITCH + (c % RC) * 8) = v[i];
+    }
+  }
+  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
+                                                      uint32_t ok) {
+    const v4u zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) v[i] = ((ok >> i) & 1u) ? v[i] : zero;
+    store(lds, v);
+  }
+  // lane l (group G = l / 16, q = l % 16) points at K-row 8 (G / 2) + q / 4,
+  // column 16 (G % 2) + 4 (q % 4) of its wave's half of the rows
+  __device__ __forceinline__ static int lane_offset(int h, int lane) {
+    return (8 * (lane >> 5) + ((lane & 15) >> 2)) * PITCH + h * (ROWS / 2) +
+           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  }
+  __device__ __forceinline__ static bf16x8 frag(const uint16_t* tile, int off, int i, int s) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const uint16_t* p = tile + off + s * 16 * PITCH + i * 32;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * PITCH));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 template <class C, bool A_KC, bool B_KC, int MODE>
 __global__ __launch_bounds__(NTHREADS, C::WPE) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LROW = C::LROW, TM = C::TM, TN = C::TN;
@@ -266,77 +375,107 @@ __global__ __launch_bounds__(NTHREADS, C::WPE) void gemm_bf16_kernel(GemmArgs g)
   }
 }
 
-// Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
-// so the wave itself must hide every latency).  Per K step (4 sub-steps of
+// Interleave one sub-step's 16 MFMAs with NR LDS fragment reads (8, 12 or
+// 16) and, when VMEM, the 16 global loads of the next tile.
+template <int NR, bool VMEM>
+__device__ __forceinline__ void sched_reads() {
+  static_assert(NR == 8 || NR == 12 || NR == 16, "reads per sub-step");
+  if constexpr (NR == 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
+    }
+  } else if constexpr (NR == 12) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+  }
+}
+
+// K loop of the pipelined kernel; EDGE selects masked loads (tiles that
+// overhang M, N or the K range) over plain ones.  Per K step (4 sub-steps of
 // 16): the next tile's global loads are issued at sub-step 0; each sub-step
 // reads the next sub-step's fragments from LDS into a second register set
 // while its 16 MFMAs run; the staged next tile is written to the other LDS
 // buffer during sub-step 2; one barrier ends the step.  The body has no
 // branches, and sched_group_barrier interleaves the memory instructions with
 // the MFMAs.
-// K loop of the pipelined kernel; EDGE selects masked loads (tiles that
-// overhang M, N or the K range) over plain ones.  Body is branch-free.
 template <class C, bool A_KC, bool B_KC, bool EDGE>
-__device__ __forceinline__ void pipe_mainloop(const GemmArgs& g, int m0, int n0, int kbeg,
-                                              int kend, uint16_t (*As)[C::BM * C::LROW],
-                                              uint16_t (*Bs)[C::BN * C::LROW],
-                                              f32x16 (&acc)[C::TM][C::TN]) {
-  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LROW = C::LROW, TM = C::TM, TN = C::TN;
+__device__ __forceinline__ void pipe_mainloop(
+    const GemmArgs& g, int m0, int n0, int kbeg, int kend,
+    uint16_t (*As)[PipeOp<C::BM, C::BK, A_KC>::ELEMS],
+    uint16_t (*Bs)[PipeOp<C::BN, C::BK, B_KC>::ELEMS], f32x16 (&acc)[C::TM][C::TN]) {
+  constexpr int BK = C::BK, TM = C::TM, TN = C::TN;
   constexpr int NS = BK / 16;
-  using SA = Stage<BM, BK, A_KC>;
-  using SB = Stage<BN, BK, B_KC>;
+  using OA = PipeOp<C::BM, BK, A_KC>;
+  using OB = PipeOp<C::BN, BK, B_KC>;
+  constexpr int NR = TM * OA::READS + TN * OB::READS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  v4u ra[SA::NREG], rb[SB::NREG];
+  v4u ra[OA::NREG], rb[OB::NREG];
   uint32_t oka = ~0u, okb = ~0u;
   auto load = [&](int k) {
     if constexpr (EDGE) {
-      SA::load_clamped(g.A, g.lda, g.M, m0, k, kend, ra, oka);
-      SB::load_clamped(g.B, g.ldb, g.N, n0, k, kend, rb, okb);
+      OA::load_clamped(g.A, g.lda, g.M, m0, k, kend, ra, oka);
+      OB::load_clamped(g.B, g.ldb, g.N, n0, k, kend, rb, okb);
     } else {
-      SA::load_interior(g.A, g.lda, m0, k, ra);
-      SB::load_interior(g.B, g.ldb, n0, k, rb);
+      OA::load_interior(g.A, g.lda, m0, k, ra);
+      OB::load_interior(g.B, g.ldb, n0, k, rb);
     }
   };
   auto store = [&](int b) {
     if constexpr (EDGE) {
-      SA::template store_masked<LROW>(As[b], ra, oka);
-      SB::template store_masked<LROW>(Bs[b], rb, okb);
+      OA::store_masked(As[b], ra, oka);
+      OB::store_masked(Bs[b], rb, okb);
     } else {
-      SA::template store<LROW>(As[b], ra);
-      SB::template store<LROW>(Bs[b], rb);
+      OA::store(As[b], ra);
+      OB::store(Bs[b], rb);
     }
   };
   load(kbeg);
   store(0);
   __syncthreads();
 
-  const int a_off = (wm * (BM / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
-  const int b_off = (wn * (BN / 2) + (lane & 31)) * LROW + 8 * (lane >> 5);
+  const int a_off = OA::lane_offset(wm, lane);
+  const int b_off = OB::lane_offset(wn, lane);
   bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(As[0] + a_off + i * 32 * LROW);
+  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(As[0], a_off, i, 0);
 #pragma unroll
-  for (int jj = 0; jj < TN; ++jj) fb[0][jj] = *reinterpret_cast<const bf16x8*>(Bs[0] + b_off + jj * 32 * LROW);
+  for (int jj = 0; jj < TN; ++jj) fb[0][jj] = OB::frag(Bs[0], b_off, jj, 0);
 
   const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
   int buf = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     // next tile (the last step reloads its own tile; that copy is never read)
     load(min(k0 + BK, last));
-    const uint16_t* a_l = As[buf] + a_off;
-    const uint16_t* b_l = Bs[buf] + b_off;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
       if (s + 1 < NS) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          fa[nxt][i] = *reinterpret_cast<const bf16x8*>(a_l + i * 32 * LROW + (s + 1) * 16);
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(As[buf], a_off, i, s + 1);
 #pragma unroll
-        for (int jj = 0; jj < TN; ++jj)
-          fb[nxt][jj] = *reinterpret_cast<const bf16x8*>(b_l + jj * 32 * LROW + (s + 1) * 16);
+        for (int jj = 0; jj < TN; ++jj) fb[nxt][jj] = OB::frag(Bs[buf], b_off, jj, s + 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -347,30 +486,17 @@ __device__ __forceinline__ void pipe_mainloop(const GemmArgs& g, int m0, int n0,
       if (s == 2) store(buf ^ 1);
       // interleave the memory instructions with the MFMAs
       if (s == 0) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-          __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
-        }
+        sched_reads<NR, true>();
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       } else if (s == 1) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        sched_reads<NR, false>();
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       } else if (s == 2) {
+        sched_reads<NR, false>();
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);   // DS write
+          __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
         }
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
@@ -379,26 +505,20 @@ __device__ __forceinline__ void pipe_mainloop(const GemmArgs& g, int m0, int n0,
     __syncthreads();
     buf ^= 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8*>(As[buf] + a_off + i * 32 * LROW);
+    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(As[buf], a_off, i, 0);
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) fb[0][jj] = *reinterpret_cast<const bf16x8*>(Bs[buf] + b_off + jj * 32 * LROW);
+    for (int jj = 0; jj < TN; ++jj) fb[0][jj] = OB::frag(Bs[buf], b_off, jj, 0);
   }
 }
 
 // Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
-// so the wave itself must hide every latency).  Per K step (4 sub-steps of
-// 16): the next tile's global loads are issued at sub-step 0; each sub-step
-// reads the next sub-step's fragments from LDS into a second register set
-// while its 16 MFMAs run; the staged next tile is written to the other LDS
-// buffer during sub-step 2; one barrier ends the step.  sched_group_barrier
-// interleaves the memory instructions with the MFMAs.
+// so the wave itself must hide every latency; see pipe_mainloop).
 template <class C, bool A_KC, bool B_KC, int MODE>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
   static_assert(BK == 64 && TM == 4 && TN == 4, "pipelined kernel expects 256 x 256 x 64");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * C::LROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * C::LROW];
-
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][PipeOp<BM, BK, A_KC>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PipeOp<BN, BK, B_KC>::ELEMS];
   const int tiles = g.tiles_m * g.tiles_n;
   const int id = blockIdx.x;
   const int q = tiles / 8, rr = tiles % 8;
@@ -497,18 +617,17 @@ hipError_t launch_large(bool a_kc, bool b_kc, int mode, const GemmArgs& g, int s
 hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g, int splits,
                      hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  // Tile choice from measurements on MI355X: with both operands K-contiguous
-  // (the logits product) the pipelined 256 x 256 tile; with a transposed
-  // operand the 256 x 128 tile at two workgroups per CU, which overlaps one
+  // Tile choice from measurements on MI355X: the pipelined 256 x 256 tile
+  // whenever it gives at least two workgroups per CU (MN-contiguous operands
+  // read through the LDS transpose); otherwise, with a transposed operand,
+  // the 256 x 128 tile at two workgroups per CU, which overlaps one
   // workgroup's staging and barrier with the other's MFMAs; small problems
   // the 128 x 128 tile.
+  const int64_t large_tiles = int64_t((g.M + 255) / 256) * ((g.N + 255) / 256) * splits;
   const int64_t mid_tiles = int64_t((g.M + 255) / 256) * ((g.N + 127) / 128) * splits;
-  if (a_kcontig && b_kcontig) {
-    const int64_t large_tiles = int64_t((g.M + 255) / 256) * ((g.N + 255) / 256) * splits;
-    if (large_tiles >= 512) return launch_large(true, true, mode, g, splits, s);
-  } else if (mid_tiles >= 512) {
+  if (large_tiles >= 512) return launch_large(a_kcontig, b_kcontig, mode, g, splits, s);
+  if (!(a_kcontig && b_kcontig) && mid_tiles >= 512)
     return launch_cfg<Mid>(a_kcontig, b_kcontig, mode, g, splits, s);
-  }
   return launch_cfg<Small>(a_kcontig, b_kcontig, mode, g, splits, s);
 }
 

@@ -12,16 +12,20 @@
 // Three block tiles, all 256 lanes = 4 waves in a 2 x 2 grid:
 //  * 256 x 256 x 64, software-pipelined (each wave 128 x 128 = 4 x 4
 //    v_mfma_f32_32x32x16_bf16, 256 accumulators per lane in AGPRs, one wave
-//    per SIMD, 144 KB of LDS) for the K-contiguous logits product;
-//  * 256 x 128 x 32 at two workgroups per CU for products with a transposed
-//    operand;
+//    per SIMD, 144 KB of LDS), used in every layout once a problem has at
+//    least 512 such tiles (all three products of the fused path);
+//  * 256 x 128 x 32 at two workgroups per CU for mid-size products with a
+//    transposed operand;
 //  * 128 x 128 x 32 for small problems.
 // Tiles are staged global -> registers -> LDS, double buffered:
 // the next tile's global loads are in flight while the current one feeds
-// the MFMAs.  LDS rows are K-contiguous with a 16-byte pad, so each lane's
-// 8-element operand fragment is one conflict-free 128-bit LDS read.  A
-// non-K-contiguous operand is transposed while staged: each lane loads two
-// K-rows of an 8 x 8 block and writes 8 (k, k+1) pairs (one v_perm_b32 each).
+// the MFMAs.  In the pipelined tile a K-contiguous operand sits in LDS as
+// [row][k] (16-byte pad; a fragment is one 128-bit read) and an
+// MN-contiguous one as [k][row], copied as is and read back transposed by
+// ds_read_b64_tr_b16 (two per fragment).  The two smaller tiles keep every
+// operand K-contiguous in LDS and transpose an MN-contiguous one while
+// staging it: each lane loads two K-rows of an 8 x 8 block and writes 8
+// (k, k+1) pairs (one v_perm_b32 each).
 //
 // Operand fragment layout of v_mfma_f32_32x32x16_bf16 (checked on MI355X):
 // lane l holds A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32],

@@ -82,6 +82,11 @@ template <> struct Vec<uint16_t> {
     v.w = pack_bf16x2(x[6], x[7]);
     return v;
   }
+  // element k (0..7, any lane-varying value) of the vector
+  __device__ __forceinline__ static float elem(const u32x4& v, int k) {
+    const uint32_t w = (k & 4) ? ((k & 2) ? v.w : v.z) : ((k & 2) ? v.y : v.x);
+    return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
@@ -94,6 +99,10 @@ template <> struct Vec<float> {
     v.x = __float_as_uint(x[0]); v.y = __float_as_uint(x[1]);
     v.z = __float_as_uint(x[2]); v.w = __float_as_uint(x[3]);
     return v;
+  }
+  // element k (0..3, any lane-varying value) of the vector
+  __device__ __forceinline__ static float elem(const u32x4& v, int k) {
+    return __uint_as_float((k & 2) ? ((k & 1) ? v.w : v.z) : ((k & 1) ? v.y : v.x));
   }
 };
 

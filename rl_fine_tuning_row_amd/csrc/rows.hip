@@ -316,6 +316,14 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   const u32x4* __restrict__ rv = reinterpret_cast<const u32x4*>(row);
   const u32x4 fill = {Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits};
 
+  static_assert(WG > 64, "the gathered logit is passed through the reduction's LDS barrier");
+  // per-row scalars first: their latency hides under the row's loads
+  const int64_t y = f.ids[r];
+  const float w = a.dloss[r];
+  const float A = f.adv[r / f.L];
+  const float old_lp = f.old_logp[r];
+  const float ref_lp = f.ref_logp != nullptr ? f.ref_logp[r] : 0.0f;
+
   u32x4 v[VPT];
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -325,6 +333,21 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   const int jt = nvec * VE + tid;  // the V % VE tail elements, one per lane
   const bool has_tail = jt < V;
   const float xt = has_tail ? load_elem(row + jt) : __uint_as_float(0xF149F2CAu);
+
+  // the lane holding column y hands z_y to the others through LDS (no re-read)
+  const bool valid = y >= 0 && y < V;
+  const int yi = valid ? int(y) : 0;
+  const int vy = yi / VE, ky = yi % VE;
+  __shared__ float sh_zy;
+  if (valid) {
+    if (vy < nvec) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (tid + i * WG == vy) sh_zy = Vec<TIn>::elem(v[i], ky);
+    } else if (has_tail && jt == yi) {
+      sh_zy = xt;
+    }
+  }
 
   // lane statistics over the registers: max first, then the sums
   float m = xt;
@@ -365,21 +388,17 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   // per-token epilogue, computed alike in every lane
   const float logS = logf(st.s);
   const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
-  const int64_t y = f.ids[r];
-  const bool valid = y >= 0 && y < V;
-  const float zy = valid ? load_elem(row + y) : __builtin_nanf("");
+  const float zy = valid ? sh_zy : __builtin_nanf("");
   const float lse = st.m / f.T + logS;
   const float logp = (zy - st.m) / f.T - logS;
   float kl = 0.0f;
   if (f.ref_logp != nullptr) {
-    const float d = f.ref_logp[r] - logp;
+    const float d = ref_lp - logp;
     kl = expm1f(d) - d;
   }
-  const float A = f.adv[r / f.L];
-  const Ppo q = ppo_terms(logp - f.old_logp[r], A, f.lo, f.hi);
-  const float w = a.dloss[r];
+  const Ppo q = ppo_terms(logp - old_lp, A, f.lo, f.hi);
   float klg = 0.0f;
-  if (f.ref_logp != nullptr && f.beta != 0.0f) klg = -f.beta * expm1f(f.ref_logp[r] - logp);
+  if (f.ref_logp != nullptr && f.beta != 0.0f) klg = -f.beta * expm1f(ref_lp - logp);
   const float g = uniform(((q.clipped ? 0.0f : -q.ratio * A) + klg) * w);
   const bool zero = (g == 0.0f);
   if (tid == 0) {
@@ -411,8 +430,6 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   }
   const float coef = g / f.T;
   const float lse2 = lse * kLog2e;
-  const int yi = int(y);
-  const int vy = yi / VE, ky = yi % VE;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int idx = tid + i * WG;
