@@ -12,6 +12,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
@@ -481,7 +482,7 @@ __device__ __forceinline__ void pipe_mainloop(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][jj],
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jj], fa[cur][i],
                                                               acc[i][jj], 0, 0, 0);
       if (s == 2) store(buf ^ 1);
       // interleave the memory instructions with the MFMAs
@@ -546,22 +547,67 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
     else pipe_mainloop<C, A_KC, B_KC, true>(g, m0, n0, kbeg, kend, As, Bs, acc);
   }
 
+  // Epilogue.  The MFMAs ran with the operands swapped (B fragment as the
+  // row operand), so accumulator r of lane l holds C[m][n] at
+  // m = 32 i + l % 32, n = 32 jj + 8 (r / 4) + 4 (l / 32) + r % 4: four
+  // consecutive columns per lane.  Each wave stages one 32 x 128 block of
+  // its 128 x 128 tile at a time in its own LDS slice (16-byte writes), reads
+  // it back as whole rows and writes C with 16-byte stores, two 512-byte
+  // rows per instruction (the accumulate mode loads C the same way first).
+  __syncthreads();  // every wave is done with the operand tiles
+  constexpr int EP = 128 + 4;  // staging pitch in floats
+  static_assert(4 * 32 * EP * 4 <= int(sizeof(As)), "staging fits the A tiles");
+  float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * (32 * EP);
   float* Cp = g.C + int64_t(z) * g.split_stride;
-  const int nl = lane & 31, mg = 4 * (lane >> 5);
+  const int mw = m0 + wm * (BM / 2), nw = n0 + wn * (BN / 2);
+  const int col = 4 * (lane & 31);
+  const int n = nw + col;
+  const bool full_n = g.vec_c && (n + 3 < g.N);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) {
-      const int n = n0 + wn * (BN / 2) + jj * 32 + nl;
-      if (n >= g.N) continue;
+    for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + mg + (r & 3);
-        if (m < g.M) {
-          float* p = Cp + int64_t(m) * g.ldc + n;
-          if constexpr (MODE == GEMM_ACCUM) *p += acc[i][jj][r];
-          else *p = acc[i][jj][r];
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                         acc[i][jj][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(stage + (lane & 31) * EP + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
+      }
+    // rows 2 u + lane / 32 of the block, columns 4 (lane % 32) .. +3
+    f32x4 cur[16];
+    if constexpr (MODE == GEMM_ACCUM) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int m = mw + 32 * i + 2 * u + (lane >> 5);
+        float* p = Cp + int64_t(m) * g.ldc + n;
+        if (m < g.M && full_n) {
+          cur[u] = *reinterpret_cast<const f32x4*>(p);
+        } else {
+          cur[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (m < g.M)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) cur[u][e] = p[e];
         }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + (2 * u + (lane >> 5)) * EP + col);
+      if constexpr (MODE == GEMM_ACCUM) cur[u] += v;
+      else cur[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int m = mw + 32 * i + 2 * u + (lane >> 5);
+      if (m >= g.M) continue;
+      float* p = Cp + int64_t(m) * g.ldc + n;
+      if (full_n) {
+        *reinterpret_cast<f32x4*>(p) = cur[u];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < g.N) p[e] = cur[u][e];
       }
     }
   }
@@ -569,6 +615,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
 
 template <class C, bool A_KC, bool B_KC>
 hipError_t launch_pipe(int mode, GemmArgs g, int splits, hipStream_t s) {
+  // 16-byte accesses to C need every row start (and split slab) 16-byte aligned
+  g.vec_c = (reinterpret_cast<uintptr_t>(g.C) % 16 == 0) && (g.ldc % 4 == 0) &&
+            (splits == 1 || g.split_stride % 4 == 0);
   g.tiles_m = (g.M + C::BM - 1) / C::BM;
   g.tiles_n = (g.N + C::BN - 1) / C::BN;
   const dim3 grid(unsigned(g.tiles_m * g.tiles_n), unsigned(splits));

@@ -50,6 +50,7 @@ struct GemmArgs {
   int32_t k_per_split;     // multiple of 64; split z covers [z*kps, min(K, (z+1)*kps))
   int64_t split_stride;    // elements between the split-K partial slabs of C
   int32_t tiles_m, tiles_n;
+  int32_t vec_c;           // C rows can take 16-byte accesses (set at launch)
 };
 
 // Enqueue one GEMM; requires K, and the contiguous extent of every operand,
