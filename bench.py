@@ -79,19 +79,25 @@ def cpu_model():
     return "unknown"
 
 
-def stored_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the stored counter runs, if the kernels have
-    not changed since (source digest)."""
+def stored_counters(workload: str):
+    """Per-kernel entries of the stored counter runs for a workload, if the
+    kernels have not changed since (source digest); else {}."""
     from rl_fine_tuning_row_amd.build import source_digest
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         data = json.load(f)
     if data.get("source_digest") != source_digest():
-        return None
-    e = data.get("kernels", {}).get(f"{workload}:{kernel}")
-    if e is None:
+        return {}
+    pre = workload + ":"
+    return {k[len(pre):]: v for k, v in data.get("kernels", {}).items() if k.startswith(pre)}
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the stored counter runs (None if stale)."""
+    e = stored_counters(workload).get(kernel)
+    if e is None or "fetch_bytes" not in e:
         return None
     return e["fetch_bytes"] + e["write_bytes"]
 
@@ -423,6 +429,11 @@ def run_fused(args, torch, grl, synth):
                      "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
     })
+    # per-product MFMA utilisation and rate from the stored rocprofv3 runs (4-sequence chunks)
+    gem = {k: v for k, v in stored_counters("fused-linear").items() if "mfma_util" in v}
+    if gem and c == 4:
+        res["gemm_counters"] = {k: {"mfma_util": v["mfma_util"], "trace_avg_us": v["trace_avg_us"],
+                                    "TFLOP/s": v["tflops"]} for k, v in gem.items()}
     if not args.no_cpu_baseline:
         import oracle
         hh = oracle.decode_bf16(case.hidden[:case.L])
