@@ -413,13 +413,15 @@ __device__ __forceinline__ void sched_reads() {
 
 // K loop of the pipelined kernel; EDGE selects masked loads (tiles that
 // overhang M, N or the K range) over plain ones.  Per K step (4 sub-steps of
-// 16): the next tile's global loads are issued at sub-step 0; each sub-step
-// reads the next sub-step's fragments from LDS into a second register set
-// while its 16 MFMAs run; the staged next tile is written to the other LDS
-// buffer during sub-step 2; one barrier ends the step.  The body has no
-// branches, and sched_group_barrier interleaves the memory instructions with
-// the MFMAs.
-template <class C, bool A_KC, bool B_KC, bool EDGE>
+// 16): each sub-step reads the next sub-step's fragments from LDS into a
+// second register set while its 16 MFMAs run; the staged next step is
+// written to the other LDS buffer during sub-step 2; one barrier ends the
+// step.  The global loads for the next step are issued at sub-step 0 (half a
+// step of latency cover), or with DEEP right after the sub-step-2 store for
+// the step after next (a full step; the prologue then loads two steps).  The
+// body has no branches, and sched_group_barrier interleaves the memory
+// instructions with the MFMAs.
+template <class C, bool A_KC, bool B_KC, bool EDGE, bool DEEP>
 __device__ __forceinline__ void pipe_mainloop(
     const GemmArgs& g, int m0, int n0, int kbeg, int kend,
     uint16_t (*As)[PipeOp<C::BM, C::BK, A_KC>::ELEMS],
@@ -452,8 +454,10 @@ __device__ __forceinline__ void pipe_mainloop(
       OB::store(Bs[b], rb);
     }
   };
+  const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
   load(kbeg);
   store(0);
+  if constexpr (DEEP) load(min(kbeg + BK, last));
   __syncthreads();
 
   const int a_off = OA::lane_offset(wm, lane);
@@ -464,11 +468,10 @@ __device__ __forceinline__ void pipe_mainloop(
 #pragma unroll
   for (int jj = 0; jj < TN; ++jj) fb[0][jj] = OB::frag(Bs[0], b_off, jj, 0);
 
-  const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
   int buf = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
     // next tile (the last step reloads its own tile; that copy is never read)
-    load(min(k0 + BK, last));
+    if constexpr (!DEEP) load(min(k0 + BK, last));
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
@@ -484,10 +487,15 @@ __device__ __forceinline__ void pipe_mainloop(
         for (int jj = 0; jj < TN; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jj], fa[cur][i],
                                                               acc[i][jj], 0, 0, 0);
-      if (s == 2) store(buf ^ 1);
+      if (s == 2) {
+        store(buf ^ 1);
+        // DEEP: the loads for two steps ahead follow the store, a full step
+        // of latency cover (the tail reloads the last step, never read)
+        if constexpr (DEEP) load(min(k0 + 2 * BK, last));
+      }
       // interleave the memory instructions with the MFMAs
       if (s == 0) {
-        sched_reads<NR, true>();
+        sched_reads<NR, !DEEP>();
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       } else if (s == 1) {
         sched_reads<NR, false>();
@@ -498,6 +506,7 @@ __device__ __forceinline__ void pipe_mainloop(
         for (int u = 0; u < 8; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
+          if constexpr (DEEP) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
         }
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
@@ -514,7 +523,7 @@ __device__ __forceinline__ void pipe_mainloop(
 
 // Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
 // so the wave itself must hide every latency; see pipe_mainloop).
-template <class C, bool A_KC, bool B_KC, int MODE>
+template <class C, bool A_KC, bool B_KC, int MODE, bool DEEP>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
   static_assert(BK == 64 && TM == 4 && TN == 4, "pipelined kernel expects 256 x 256 x 64");
@@ -543,8 +552,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
 
   if (kend > kbeg) {
     const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && ((kend - kbeg) % BK == 0);
-    if (interior) pipe_mainloop<C, A_KC, B_KC, false>(g, m0, n0, kbeg, kend, As, Bs, acc);
-    else pipe_mainloop<C, A_KC, B_KC, true>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    if (interior) pipe_mainloop<C, A_KC, B_KC, false, DEEP>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    else pipe_mainloop<C, A_KC, B_KC, true, DEEP>(g, m0, n0, kbeg, kend, As, Bs, acc);
   }
 
   // Epilogue.  The MFMAs ran with the operands swapped (B fragment as the
@@ -621,10 +630,14 @@ hipError_t launch_pipe(int mode, GemmArgs g, int splits, hipStream_t s) {
   g.tiles_m = (g.M + C::BM - 1) / C::BM;
   g.tiles_n = (g.N + C::BN - 1) / C::BN;
   const dim3 grid(unsigned(g.tiles_m * g.tiles_n), unsigned(splits));
+  // loads two steps ahead where it measured faster: products with an
+  // MN-contiguous operand (dz W and dz^T h, 64 and ~300 K steps per tile);
+  // the logits product (16 steps per tile) keeps the one-step form
+  constexpr bool DEEP = !(A_KC && B_KC);
   if (mode == GEMM_ACCUM)
-    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_ACCUM>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_ACCUM, DEEP>), grid, dim3(NTHREADS), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_STORE>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_STORE, DEEP>), grid, dim3(NTHREADS), 0, s, g);
   return hipGetLastError();
 }
 
