@@ -230,7 +230,12 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  *   grad_hidden = dz * weight            (overwritten, fp32 [R, H]),
  *   grad_weight += dz^T * hidden         (accumulated, fp32 [V, H]),
  * with dz rounded to bf16 before the two products.  The caller loops over
- * chunks; level must be GRPO_TOKEN.
+ * chunks; level must be GRPO_TOKEN.  Rows whose dloss is exactly 0 (padding,
+ * masked tokens) add nothing to any output and are not computed: they are
+ * compacted away on the device before the first product (the zero-gradient
+ * skip of [LIGER-BWD "Why is this good"] applied to the chunk), their
+ * grad_hidden rows are written as 0, and non-finite inputs on them do not
+ * propagate.  mask is not read (dloss carries it at token level).
  *
  * hidden bf16 [R, H] row-major; weight bf16 [V, H] row-major (in)
  * ids, old_logp, ref_logp (nullable), mask (nullable), dloss: [R] (in)
@@ -239,7 +244,8 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  * grad_weight fp32 [V, H] (in/out)
  * workspace: device buffer of at least
  *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned; it
- *   holds the chunk's fp32 logits and bf16 dlogits (about 6 R V bytes).
+ *   holds the chunk's fp32 logits and bf16 dlogits (about 6 R V bytes) and
+ *   the compacted rows' hidden states and inputs (about 2 R H + 32 R).
  * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,
  * weight and grad_hidden 16-byte aligned.  The result is deterministic.
  * ------------------------------------------------------------------------ */

@@ -5,13 +5,24 @@
 // during the forward and accumulated, so the whole batch's logits never
 // exist ["Liger GRPO meets TRL" summary, detailed items 3 and 4].  Per chunk
 // of R = nseq * L rows, all on the caller's stream:
-//   1. z  = h W^T                 MFMA GEMM, fp32 [R, V] in the workspace
+//   0. compaction                 the rows whose weight dloss is nonzero, in
+//                                 order (one workgroup), their h rows and
+//                                 per-row inputs gathered; Rc of them
+//   1. z  = h_c W^T               MFMA GEMM, fp32 [Rc, V] in the workspace
 //   2. row forward on z           lse, logp, per-token loss (fp32 rows)
-//   3. row backward on z          dz = g/T (onehot - p) as bf16 [R, V]
+//   3. row backward on z          dz = g/T (onehot - p) as bf16 [Rc, V]
 //   4. loss_accum += sum dloss * loss     (one workgroup, fixed order)
 //   5. grad_hidden = dz W         MFMA GEMM split over V, partial sums reduced
-//                                 in a fixed order (deterministic)
-//   6. grad_weight += dz^T h      MFMA GEMM accumulating into fp32
+//                                 in a fixed order (deterministic) and
+//                                 scattered back; dropped rows get 0
+//   6. grad_weight += dz^T h_c    MFMA GEMM accumulating into fp32
+// A row with dloss = 0 (padding, a masked token) adds 0 to the loss and its
+// dlogp, hence its dz row and its grad_hidden row, is 0: skipping it is the
+// zero-gradient skip of the logits backward ["[Liger-Kernel] LinkedIn
+// Liger-Kernel GRPO Loss Backward optimisation", Why is this good] carried
+// into the chunked products.  (Non-finite inputs on such a row are dropped
+// with it instead of propagating through 0 * inf.)  Rc is only known on the
+// device: every later launch is sized for R and reads Rc there.
 // z stays fp32 so the per-token loss meets a 1e-5 relative bar; dz is
 // rounded to bf16 before the two products (the matrix cores' input type).
 #include <hip/hip_runtime.h>
@@ -30,7 +41,9 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t z_off, dz_off, logp_off, lse_off, loss_off, total;
+  size_t z_off, dz_off, logp_off, lse_off, loss_off;
+  size_t map_off, pos_off, cnt_off, hc_off, ids_off, old_off, ref_off, adv_off, w_off;
+  size_t total;
   int splits;
 };
 
@@ -47,19 +60,96 @@ WsLayout ws_layout(int64_t R, int64_t V, int64_t H) {
   WsLayout w{};
   w.splits = pick_splits(R, H);
   const size_t zb = size_t(R) * size_t(V) * 4;
-  const size_t part = w.splits > 1 ? size_t(w.splits) * size_t(R) * size_t(H) * 4 : 0;
-  w.z_off = 0;  // z, later reused for the split-K partial sums
-  w.dz_off = align256(std::max(zb, part));
-  w.logp_off = w.dz_off + align256(size_t(R) * size_t(V) * 2);
-  w.lse_off = w.logp_off + align256(size_t(R) * 4);
-  w.loss_off = w.lse_off + align256(size_t(R) * 4);
-  w.total = w.loss_off + align256(size_t(R) * 4);
+  const size_t part = size_t(w.splits) * size_t(R) * size_t(H) * 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  w.z_off = take(std::max(zb, part));  // z, later reused for the split-K partial sums
+  w.dz_off = take(size_t(R) * size_t(V) * 2);
+  w.logp_off = take(size_t(R) * 4);
+  w.lse_off = take(size_t(R) * 4);
+  w.loss_off = take(size_t(R) * 4);
+  w.map_off = take(size_t(R) * 4);
+  w.pos_off = take(size_t(R) * 4);
+  w.cnt_off = take(4);
+  w.hc_off = take(size_t(R) * size_t(H) * 2);
+  w.ids_off = take(size_t(R) * 8);
+  w.old_off = take(size_t(R) * 4);
+  w.ref_off = take(size_t(R) * 4);
+  w.adv_off = take(size_t(R) * 4);
+  w.w_off = take(size_t(R) * 4);
+  w.total = o;
   return w;
 }
 
+// Compaction of the rows with nonzero weight, in order, by one workgroup:
+// map[i] = original row of compact row i, pos[r] = compact index of row r or
+// -1, *count = number kept; the kept rows' per-row inputs are gathered
+// (advantage per row, so the compact problem has one token per "sequence").
+// NaN weights are kept (NaN != 0).
+__global__ __launch_bounds__(1024) void compact_rows_kernel(
+    int R, int L, const float* __restrict__ dloss, const int64_t* __restrict__ ids,
+    const float* __restrict__ old_logp, const float* __restrict__ ref_logp,
+    const float* __restrict__ adv, int32_t* __restrict__ map, int32_t* __restrict__ pos,
+    int32_t* __restrict__ count, int64_t* __restrict__ ids_c, float* __restrict__ old_c,
+    float* __restrict__ ref_c, float* __restrict__ adv_c, float* __restrict__ w_c) {
+  __shared__ int wave_tot[16];
+  __shared__ int base_sh;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t == 0) base_sh = 0;
+  __syncthreads();
+  for (int r0 = 0; r0 < R; r0 += 1024) {
+    const int r = r0 + t;
+    const float w = r < R ? dloss[r] : 0.0f;
+    const bool keep = r < R && w != 0.0f;
+    const uint64_t bal = __ballot(keep);
+    const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) wave_tot[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base_sh;
+    for (int k = 0; k < wave; ++k) off += wave_tot[k];
+    const int i = off + below;
+    if (r < R) pos[r] = keep ? i : -1;
+    if (keep) {
+      map[i] = r;
+      ids_c[i] = ids[r];
+      old_c[i] = old_logp[r];
+      ref_c[i] = ref_logp != nullptr ? ref_logp[r] : 0.0f;
+      adv_c[i] = adv[r / L];
+      w_c[i] = w;
+    }
+    __syncthreads();  // every lane has read base_sh and wave_tot
+    if (t == 0) {
+      int tot = 0;
+      for (int k = 0; k < 16; ++k) tot += wave_tot[k];
+      base_sh += tot;
+    }
+    __syncthreads();
+  }
+  if (t == 0) *count = base_sh;
+}
+
+// h_c[i] = h[map[i]] for the kept rows; one workgroup per compact row,
+// H % 8 == 0 (16-byte vectors)
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ h, int H,
+                                                          const int32_t* __restrict__ map,
+                                                          const int32_t* __restrict__ count,
+                                                          uint16_t* __restrict__ h_c) {
+  const int i = blockIdx.x;
+  if (i >= *count) return;
+  const uint4* src = reinterpret_cast<const uint4*>(h + int64_t(map[i]) * H);
+  uint4* dst = reinterpret_cast<uint4*>(h_c + int64_t(i) * H);
+  for (int v = threadIdx.x; v < H / 8; v += 256) dst[v] = src[v];
+}
+
 __global__ __launch_bounds__(1024) void weighted_sum_kernel(const float* __restrict__ loss,
-                                                            const float* __restrict__ w, int n,
+                                                            const float* __restrict__ w,
+                                                            const int32_t* __restrict__ count,
                                                             float* __restrict__ acc) {
+  const int n = *count;
   float s = 0.0f;
   for (int i = threadIdx.x; i < n; i += 1024) s += w[i] * loss[i];
   s = wave_sum(s);
@@ -74,22 +164,31 @@ __global__ __launch_bounds__(1024) void weighted_sum_kernel(const float* __restr
   }
 }
 
-// out[i] = sum_z part[z * stride + i], z in order; n is a multiple of 4
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
-                                                            int splits, int64_t n,
-                                                            int64_t stride,
-                                                            float* __restrict__ out) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  float4 s = *reinterpret_cast<const float4*>(part + i);
-  for (int z = 1; z < splits; ++z) {
-    const float4 v = *reinterpret_cast<const float4*>(part + int64_t(z) * stride + i);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+// grad_hidden row r = sum over splits z (in order) of the partial rows of its
+// compact index pos[r], or 0 for a dropped row; H % 4 == 0
+__global__ __launch_bounds__(256) void splitk_scatter_kernel(const float* __restrict__ part,
+                                                             int splits, int64_t stride,
+                                                             const int32_t* __restrict__ pos,
+                                                             int64_t R, int H,
+                                                             float* __restrict__ out) {
+  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e >= R * H) return;
+  const int64_t r = e / H;
+  const int c = int(e % H);
+  const int p = pos[r];
+  float4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p >= 0) {
+    const int64_t i = int64_t(p) * H + c;
+    s = *reinterpret_cast<const float4*>(part + i);
+    for (int z = 1; z < splits; ++z) {
+      const float4 v = *reinterpret_cast<const float4*>(part + int64_t(z) * stride + i);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
   }
-  *reinterpret_cast<float4*>(out + i) = s;
+  *reinterpret_cast<float4*>(out + e) = s;
 }
 
 int check_fused(const void* hidden, int64_t nseq, int64_t L, int64_t H, const void* weight,
@@ -146,12 +245,28 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   float* logp = reinterpret_cast<float*>(base + w.logp_off);
   float* lse = reinterpret_cast<float*>(base + w.lse_off);
   float* loss = reinterpret_cast<float*>(base + w.loss_off);
+  int32_t* map = reinterpret_cast<int32_t*>(base + w.map_off);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + w.pos_off);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt_off);
+  uint16_t* h_c = reinterpret_cast<uint16_t*>(base + w.hc_off);
+  int64_t* ids_c = reinterpret_cast<int64_t*>(base + w.ids_off);
+  float* old_c = reinterpret_cast<float*>(base + w.old_off);
+  float* ref_c = reinterpret_cast<float*>(base + w.ref_off);
+  float* adv_c = reinterpret_cast<float*>(base + w.adv_off);
+  float* w_c = reinterpret_cast<float*>(base + w.w_off);
   const uint16_t* h = static_cast<const uint16_t*>(hidden);
   const uint16_t* W = static_cast<const uint16_t*>(weight);
 
-  // 1. logits of the chunk
+  // 0. the rows that carry weight, and their inputs
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, s, int(R), int(L), dloss, ids,
+                     old_logp, ref_logp, adv, map, pos, cnt, ids_c, old_c, ref_c, adv_c, w_c);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(unsigned(R)), dim3(256), 0, s, h, int(H), map, cnt,
+                     h_c);
+  if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
+
+  // 1. logits of the kept rows
   GemmArgs g1{};
-  g1.A = h;
+  g1.A = h_c;
   g1.lda = H;
   g1.B = W;
   g1.ldb = H;
@@ -161,18 +276,19 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   g1.N = int32_t(V);
   g1.K = int32_t(H);
   g1.k_per_split = int32_t(H);
+  g1.dev_m = cnt;
   if (gemm_bf16(true, true, GEMM_STORE, g1, 1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
 
-  // 2. forward row pass on the fp32 logits
+  // 2. forward row pass on the fp32 logits (compact rows: one token per "sequence")
   FwdArgs fa{};
   fa.logits = z;
   fa.ld = V;
   fa.V = int32_t(V);
-  fa.L = int32_t(L);
-  fa.ids = ids;
-  fa.old_logp = old_logp;
-  fa.ref_logp = ref_logp;
-  fa.adv = adv;
+  fa.L = 1;
+  fa.ids = ids_c;
+  fa.old_logp = old_c;
+  fa.ref_logp = ref_logp != nullptr ? ref_c : nullptr;
+  fa.adv = adv_c;
   fa.T = p->temperature;
   fa.c = kLog2e / p->temperature;
   fa.beta = p->beta;
@@ -183,6 +299,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   fa.loss = loss;
   fa.logp = logp;
   fa.lse = lse;
+  fa.dev_rows = cnt;
   st = launch_fwd(fa, GRPO_F32, R, false, s);
   if (st != GRPO_OK) return st;
 
@@ -193,15 +310,15 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   ba.dlogits = dz;
   ba.ld_out = V;
   ba.V = int32_t(V);
-  ba.L = int32_t(L);
-  ba.ids = ids;
-  ba.old_logp = old_logp;
-  ba.ref_logp = ref_logp;
-  ba.adv = adv;
-  ba.mask = mask;
+  ba.L = 1;
+  ba.ids = ids_c;
+  ba.old_logp = old_c;
+  ba.ref_logp = fa.ref_logp;
+  ba.adv = adv_c;
+  ba.mask = nullptr;
   ba.logp = logp;
   ba.lse = lse;
-  ba.dloss = dloss;
+  ba.dloss = w_c;
   ba.T = fa.T;
   ba.c = fa.c;
   ba.beta = fa.beta;
@@ -209,15 +326,16 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   ba.hi = fa.hi;
   ba.mode = BWD_GRPO;
   ba.level = GRPO_TOKEN;
+  ba.dev_rows = cnt;
   st = launch_bwd_f32_to_bf16(ba, R, s);
   if (st != GRPO_OK) return st;
 
   // 4. loss of the chunk
-  hipLaunchKernelGGL(weighted_sum_kernel, dim3(1), dim3(1024), 0, s, loss, dloss, int(R),
-                     loss_accum);
+  hipLaunchKernelGGL(weighted_sum_kernel, dim3(1), dim3(1024), 0, s, loss, w_c, cnt, loss_accum);
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
 
-  // 5. grad_hidden = dz W, split over V; partial sums reuse the z region
+  // 5. grad_hidden = dz W, split over V into partial sums (the z region),
+  //    reduced in order and scattered to the original rows
   GemmArgs g2{};
   g2.A = dz;
   g2.lda = V;
@@ -229,21 +347,22 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   const int64_t per = (V + w.splits - 1) / w.splits;
   g2.k_per_split = int32_t(((per + 63) / 64) * 64);
   g2.split_stride = R * H;
-  g2.C = w.splits > 1 ? z : grad_hidden;
+  g2.C = z;
   g2.ldc = H;
+  g2.dev_m = cnt;
   if (gemm_bf16(true, false, GEMM_STORE, g2, w.splits, s) != hipSuccess) return GRPO_ERR_LAUNCH;
-  if (w.splits > 1) {
+  {
     const int64_t n = R * H;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0,
-                       s, z, w.splits, n, n, grad_hidden);
+    hipLaunchKernelGGL(splitk_scatter_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0,
+                       s, z, w.splits, n, pos, R, int(H), grad_hidden);
     if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
   }
 
-  // 6. grad_weight += dz^T h
+  // 6. grad_weight += dz^T h_c over the kept rows
   GemmArgs g3{};
   g3.A = dz;
   g3.lda = V;
-  g3.B = h;
+  g3.B = h_c;
   g3.ldb = H;
   g3.C = grad_weight;
   g3.ldc = H;
@@ -251,6 +370,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   g3.N = int32_t(H);
   g3.K = int32_t(R);
   g3.k_per_split = int32_t(((R + 63) / 64) * 64);
+  g3.dev_k = cnt;
   if (gemm_bf16(false, false, GEMM_ACCUM, g3, 1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
   return GRPO_OK;
 }

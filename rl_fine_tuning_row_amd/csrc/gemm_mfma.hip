@@ -300,6 +300,10 @@ __global__ __launch_bounds__(NTHREADS, C::WPE) void gemm_bf16_kernel(GemmArgs g)
   const int t = xcd * q + min(xcd, rr) + j;
   const int tm = t % g.tiles_m, tn = t / g.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
+  // extents read on the device (compacted rows): tiles past them have no work
+  if (g.dev_m != nullptr) g.M = min(g.M, *g.dev_m);
+  if (g.dev_k != nullptr) g.K = min(g.K, *g.dev_k);
+  if (m0 >= g.M) return;
 
   const int z = blockIdx.y;
   const int kbeg = z * g.k_per_split;
@@ -536,6 +540,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   const int t = xcd * q + min(xcd, rr) + j;
   const int tm = t % g.tiles_m, tn = t / g.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
+  // extents read on the device (compacted rows): tiles past them have no work
+  if (g.dev_m != nullptr) g.M = min(g.M, *g.dev_m);
+  if (g.dev_k != nullptr) g.K = min(g.K, *g.dev_k);
+  if (m0 >= g.M) return;
   const int z = blockIdx.y;
   const int kbeg = z * g.k_per_split;
   const int kend = min(g.K, kbeg + g.k_per_split);

@@ -51,11 +51,18 @@ struct GemmArgs {
   int64_t split_stride;    // elements between the split-K partial slabs of C
   int32_t tiles_m, tiles_n;
   int32_t vec_c;           // C rows can take 16-byte accesses (set at launch)
+  const int32_t* dev_m;    // nullable: M is min(M, *dev_m), read on the device
+  const int32_t* dev_k;    // nullable: K is min(K, *dev_k), read on the device
 };
 
 // Enqueue one GEMM; requires K, and the contiguous extent of every operand,
 // to be multiples of 8 (16-byte chunks), lda/ldb multiples of 8, 16-byte
 // aligned A and B.  splits > 1 writes partial sums to C + z * split_stride.
+// With dev_m / dev_k the host's M / K are upper bounds (the grid is sized
+// for them) and the device reads the actual extent: rows of C past it are
+// not written, K past it is not summed.  A device K must keep the
+// K-contiguous operands' K a multiple of 8 (an MN-contiguous operand takes
+// any K).
 hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g, int splits,
                      hipStream_t s);
 

@@ -74,6 +74,7 @@ __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, flo
 template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
 __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
   const int64_t r = blockIdx.x;
+  if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
   const Stat st = block_reduce_stat<WG, NEED_T>(
       scan_row<TIn, WG, UNROLL, VEC, NEED_T, NTL>(row, a.V, a.c), a.c);
@@ -205,6 +206,7 @@ __device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float va
 template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC>
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   const int64_t r = blockIdx.x;
+  if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const float g = uniform(row_dlogp<TIn, WG>(a, r));
   const int64_t y = a.ids[r];
   const bool valid = y >= 0 && y < a.V;

@@ -29,6 +29,7 @@ struct FwdArgs {
   uint8_t* is_clipped;
   float* gathered;
   int32_t* err_count;
+  const int32_t* dev_rows;  // nullable: rows at or past *dev_rows are skipped
 };
 
 struct BwdArgs {
@@ -50,6 +51,7 @@ struct BwdArgs {
   float T, c, beta, lo, hi;
   int32_t mode, level, force_dense;
   uint8_t* zero_row;
+  const int32_t* dev_rows;  // nullable: rows at or past *dev_rows are skipped
 };
 
 struct SeqArgs {

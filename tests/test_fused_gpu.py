@@ -181,3 +181,73 @@ def test_fused_full_size(chunk):
         dzv[hit] += g[hit] / T
         want = dzv @ h
         assert _frob(gWn[k], want) <= 1e-2, (v, _frob(gWn[k], want))
+
+
+def _fused_case_with_gaps(B=4, L=40, H=128, V=392):
+    """Small case whose weights are 0 on trailing padding and also on rows in
+    the middle of sequences (every third valid token) and on the first token
+    of sequence 1."""
+    case = synth.fused_case(B=B, L=L, H=H, V=V, dloss="sum")
+    w = case.dloss.copy()
+    valid = np.flatnonzero(w != 0.0)
+    w[valid[::3]] = 0.0
+    w[L] = 0.0
+    case.dloss = w
+    return case
+
+
+@pytest.mark.parametrize("chunk", [1, 3])
+def test_fused_skips_zero_weight_rows(chunk):
+    """Rows with dloss == 0 are compacted away: results match the oracle (which
+    computes every row and multiplies by the weight), their grad_hidden rows
+    are exactly 0, and a NaN old_logp or an out-of-range id on such a row does
+    not reach any output."""
+    lib = require_gpu()
+    case = _fused_case_with_gaps()
+    say(f"fused-linear zero-weight rows skipped: chunk {chunk}, "
+        f"{int((case.dloss == 0).sum())} of {case.N} rows have weight 0")
+    h = oracle.decode_bf16(case.hidden)
+    W = oracle.decode_bf16(case.weight)
+    logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
+    old, ref = _fused_inputs(case, logp_true)
+    l_o, gh_o, gW_o = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
+                                               ref.astype(np.float64), case.adv, case.mask,
+                                               case.dloss, case.B, case.L, case.temperature,
+                                               case.beta, case.eps_low, case.eps_high, chunk)
+    dropped = np.flatnonzero(case.dloss == 0.0)
+    poisoned_old = old.copy()
+    poisoned_old[dropped[0]] = np.nan
+    ids_bad = case.ids.copy()
+    ids_bad[dropped[1]] = case.V + 7
+    case.ids = ids_bad
+    loss, gh, gW = _run_fused(lib, case, poisoned_old, ref, chunk)
+    assert np.isfinite(loss) and abs(loss - l_o) <= 1e-5 * abs(l_o) + 1e-6, (loss, l_o)
+    assert _frob(gh, gh_o) <= 1e-2, _frob(gh, gh_o)
+    assert _frob(gW.cpu().numpy(), gW_o) <= 1e-2
+    assert (gh[dropped] == 0.0).all()
+
+
+def test_fused_all_rows_zero_weight():
+    """A chunk whose weights are all 0 leaves loss_accum and grad_weight as they
+    were (bit for bit) and writes grad_hidden = 0."""
+    lib = require_gpu()
+    case = synth.fused_case(B=2, L=16, H=64, V=256, dloss="sum")
+    say("fused-linear chunk with every weight 0")
+    T = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+             eps_high=case.eps_high)
+    rng = np.random.default_rng(3)
+    gW0 = rng.standard_normal((case.V, case.H)).astype(np.float32)
+    gW = dev(gW0)
+    loss = dev(np.array([1.25], dtype=np.float32))
+    gh = dev(np.full((case.N, case.H), 7.0, dtype=np.float32))
+    ws = torch.empty(lib.fused_linear_grpo_workspace_bytes(case.N, case.V, case.H),
+                     dtype=torch.uint8, device="cuda")
+    lp = np.zeros(case.N, dtype=np.float32)
+    lib.fused_linear_grpo_chunk(_t(case.hidden), _t(case.weight), dev(case.ids), dev(lp),
+                                dev(case.adv), dev(case.mask), dev(np.zeros(case.N, np.float32)),
+                                case.B, case.L, ref_logp=dev(lp), loss_accum=loss,
+                                grad_hidden=gh, grad_weight=gW, workspace=ws, **T)
+    torch.cuda.synchronize()
+    assert float(loss.item()) == 1.25
+    assert (gh.cpu().numpy() == 0.0).all()
+    assert np.array_equal(gW.cpu().numpy(), gW0)
