@@ -203,7 +203,7 @@ __device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float va
   }
 }
 
-template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC>
+template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC, bool NTL>
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   const int64_t r = blockIdx.x;
   if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
     for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
       u32x4 v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) v[u] = load16<false>(rv + i + u * WG);
+      for (int u = 0; u < UNROLL; ++u) v[u] = load16<NTL>(rv + i + u * WG);
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         float x[VE];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
     }
     for (; i < nvec; i += WG) {
       float x[VE];
-      Vec<TIn>::unpack(load16<false>(rv + i), x);
+      Vec<TIn>::unpack(load16<NTL>(rv + i), x);
 #pragma unroll
       for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
       if (i == vy) {
@@ -515,16 +515,20 @@ hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s)
 }
 
 template <typename TIn, typename TOut, bool VEC>
-hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, bool ntl, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false>), dim3(unsigned(rows)),
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false, false>), dim3(unsigned(rows)),
                        dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
 #define X(W, U)                                                                          \
   if (sh.wg == W && sh.unroll == U) {                                                     \
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true>), dim3(unsigned(rows)),     \
-                       dim3(W), 0, s, a);                                                 \
+    if (ntl)                                                                              \
+      hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, true>),                   \
+                         dim3(unsigned(rows)), dim3(W), 0, s, a);                         \
+    else                                                                                  \
+      hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, false>),                  \
+                         dim3(unsigned(rows)), dim3(W), 0, s, a);                         \
     return hipGetLastError();                                                             \
   }
     GRPO_SHAPES(X)
@@ -550,8 +554,12 @@ hipError_t launch_fwd_dt(const FwdArgs& a, int64_t rows, Shape sh, bool vec, boo
 }
 
 // Logits matrices larger than this are read with non-temporal loads by the
-// forward-type kernels: they cannot stay in the 256 MB last-level cache for
-// a following backward anyway, and streaming them past it measured faster.
+// forward-type kernels and by the fp32 -> bf16 backward of the fused path:
+// they cannot stay in the 256 MB last-level cache between the passes
+// anyway, and streaming them past it measured faster (forward +8-12%, the
+// fp32 backward a few percent; the same-dtype backward measured 3-5%
+// slower with them and keeps normal loads).  Smaller matrices keep normal
+// loads, so the backward re-reads the forward's rows from that cache.
 constexpr int64_t kNtLoadBytes = int64_t(192) << 20;
 
 int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s) {
@@ -569,11 +577,12 @@ int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
   const Shape sh = pick_bwd_shape(rows, a.V, es);
   const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
+  const bool ntl = false;  // same-dtype backward: normal loads measured faster
   hipError_t e;
-  if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, uint16_t, true>(a, rows, sh, s)
-                                  : launch_bwd_t<uint16_t, uint16_t, false>(a, rows, sh, s);
-  else e = vec ? launch_bwd_t<float, float, true>(a, rows, sh, s)
-               : launch_bwd_t<float, float, false>(a, rows, sh, s);
+  if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, uint16_t, true>(a, rows, sh, ntl, s)
+                                  : launch_bwd_t<uint16_t, uint16_t, false>(a, rows, sh, ntl, s);
+  else e = vec ? launch_bwd_t<float, float, true>(a, rows, sh, ntl, s)
+               : launch_bwd_t<float, float, false>(a, rows, sh, ntl, s);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
@@ -638,8 +647,9 @@ int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s) {
   // fp32 rows in 16-byte vectors, bf16 rows in 8-byte vectors
   const bool vec = rows_vec_ok(a.logits, a.ld, 4) && aligned(a.dlogits, 8) &&
                    ((a.ld_out * 2) % 8) == 0;
-  const hipError_t e = vec ? launch_bwd_t<float, uint16_t, true>(a, rows, sh, s)
-                           : launch_bwd_t<float, uint16_t, false>(a, rows, sh, s);
+  const bool ntl = rows * a.ld * 4 > kNtLoadBytes;
+  const hipError_t e = vec ? launch_bwd_t<float, uint16_t, true>(a, rows, sh, ntl, s)
+                           : launch_bwd_t<float, uint16_t, false>(a, rows, sh, ntl, s);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
