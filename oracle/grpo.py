@@ -286,3 +286,67 @@ def fused_linear_loss(hidden, weight, ids, old_logp, ref_logp, adv, mask, dloss,
     fwd = grpo_forward(z, ids, old_logp, ref_logp, adv, mask, B, L, temperature, beta,
                        eps_low, eps_high, "token")
     return float((np.asarray(dloss, np.float64) * fwd["loss"]).sum())
+
+
+# ---------------------------------------------------------------------------
+# steps either side of the row pass
+# ---------------------------------------------------------------------------
+def entropy_from_logits_bwd(z: np.ndarray, grad_entropy: np.ndarray,
+                            temperature: float = 1.0) -> np.ndarray:
+    """Gradient of sum_r g_r H_r with H_r the entropy of softmax(z_r / T)
+    [AXOLOTL part 1 defines H = -sum p log p; the pages give it no backward].
+
+    With u = z / T and log p = u - lse: dH/du_j = -p_j (log p_j + H), so
+    dz_j = -(g / T) p_j (log p_j + H).  Written out from the definition with a
+    two-pass softmax; rows with g = 0 get exact zeros."""
+    u, lse = log_softmax_stats(z, temperature)
+    logp = u - lse[:, None]
+    p = np.exp(logp)
+    H = -(p * logp).sum(axis=1)
+    g = np.asarray(grad_entropy, dtype=np.float64)
+    dz = -(g / np.float64(temperature))[:, None] * p * (logp + H[:, None])
+    dz[g == 0.0] = 0.0
+    return dz
+
+
+def group_advantages(rewards: np.ndarray, group_size: int, eps: float = 1e-4,
+                     scale: bool = True) -> np.ndarray:
+    """Group-relative advantages of consecutive groups of `group_size`
+    completions (one prompt each).
+
+    The pages only name zero-advantage sequences [LIGER-BWD, summary]; they
+    give no formula.  Reading (the plain meaning of "group-relative"): centre
+    each group on its mean and, with `scale`, divide by the group's sample
+    standard deviation (n - 1) plus eps.  A group whose rewards are all equal
+    -- the zero-advantage case -- gets exactly 0 (the mean of equal floats can
+    round away from them); a group of one has no spread and also gets 0."""
+    r = np.asarray(rewards, dtype=np.float64).reshape(-1, group_size)
+    out = np.zeros_like(r)
+    for k in range(r.shape[0]):
+        g = r[k]
+        if g.max() == g.min():
+            continue
+        c = g - g.mean()
+        out[k] = c / (g.std(ddof=1) + eps) if scale else c
+    return out.reshape(-1)
+
+
+def loss_weights(mask, B: int, L: int, reduction: str) -> np.ndarray:
+    """Per-token upstream weights dloss = d(loss)/d(loss_bt) of a reduction
+    of the per-token losses (NULL mask = all ones).
+
+    The kernels take these weights as an input [LIGER-BWD "Code analysis":
+    the backward scales by dloss]; the pages do not say which reduction.
+    Readings: "token"     L = sum m l / max(sum m, 1)       (the harness's),
+              "sequence"  L = (1/B) sum_b sum_t m l / max(n_b, 1),
+              "constant"  L = sum m l / (B L)."""
+    m = (np.ones(B * L) if mask is None else np.asarray(mask, dtype=np.float64)).reshape(B, L)
+    if reduction == "token":
+        w = m / max(m.sum(), 1.0)
+    elif reduction == "sequence":
+        w = m / (np.maximum(m.sum(axis=1, keepdims=True), 1.0) * B)
+    elif reduction == "constant":
+        w = m / float(B * L)
+    else:
+        raise ValueError(reduction)
+    return w.reshape(-1)
