@@ -20,12 +20,15 @@ Other workloads (each prints its own line; not the headline):
   rows          entropy_from_logits + selective_log_softmax fwd + bwd,
                 65536 x 32000 bf16 (contiguous; --strided: rows of a 2V buffer)
   fused-linear  chunked fused-linear loss over h [32768, 1024] and
-                W [151936, 1024] bf16, --chunk sequences per call
+                W [151936, 1024] bf16, --chunk sequences per call (value:
+                rows/s; roofline on the GEMM flops executed, zero-weight
+                rows being skipped)
+  entropy-bwd   entropy_from_logits_bwd over the rows workload's logits,
+                plus the latency of grpo_group_advantages / grpo_loss_weights
 
 Inputs are synthetic, generated on the host and already resident in device
 memory when the timed region starts.  ``value`` is GB/s of algorithmic HBM
-bytes (TFLOP/s of the three products for fused-linear) over the wall time of
-the timed steps.  ``roofline`` is for the step's dominant kernel, its
+bytes (rows/s for fused-linear) over the wall time of the timed steps.  ``roofline`` is for the step's dominant kernel, its
 duration timed with events on the launch stream over back-to-back launches; ``traffic`` is the HBM bytes
 per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored in
 profiles/counters.json, used only while the kernels' source digest matches.
@@ -55,7 +58,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="grpo-token",
-                    choices=["grpo-token", "grpo-seq", "rows", "fused-linear"])
+                    choices=["grpo-token", "grpo-seq", "rows", "fused-linear", "entropy-bwd"])
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--chunk", type=int, default=4)
     ap.add_argument("--strided", action="store_true")
@@ -379,6 +382,84 @@ def run_rows(args, torch, grl, synth):
 
 
 # ---------------------------------------------------------------------------
+# steps either side of the row pass: entropy backward, advantages, weights
+# ---------------------------------------------------------------------------
+def run_entropy_bwd(args, torch, grl, synth):
+    """entropy_from_logits_bwd over the rows workload's logits (lse and H from
+    the forwards, upstream grad N(0, 1): every row dense), plus the latency
+    of grpo_group_advantages and grpo_loss_weights at the headline's sizes."""
+    case = synth.row_case()
+    N, V = case.N, case.V
+    z = torch.from_numpy(case.logits.view(np.int16)).view(torch.bfloat16).cuda()
+    ids = torch.from_numpy(case.ids).cuda()
+    grad = torch.from_numpy(case.grad).cuda()
+    _, lse = grl.selective_log_softmax(z, ids)
+    H = grl.entropy_from_logits(z)
+    dz = torch.empty((N, V), dtype=torch.bfloat16, device="cuda")
+    L = grl.lib()
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def chk(st):
+        if st != 0:
+            raise grl.GrpoError("entropy_from_logits_bwd", st)
+    f_bwd = lambda: chk(L.entropy_from_logits_bwd(P(z), 1, N, V, V, 1.0, P(lse), P(H), P(grad),
+                                                  P(dz), V, s))
+    for _ in range(max(1, args.warmup)):
+        f_bwd()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 20))
+    args.steps = steps
+    ms = timed([f_bwd], steps, torch)
+    (kt,) = kernel_times([[f_bwd]], steps, torch)
+    n_nz = int((case.grad != 0).sum())
+    nbytes = n_nz * V * 2 + N * V * 2 + N * 12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    kgbs = nbytes / (kt * 1e-3) / 1e9
+    # the two small kernels, at the headline's B=4, L=512 (one group of 4)
+    rewards = torch.tensor([1.0, 0.0, 1.0, 1.0], device="cuda")
+    adv = torch.empty(4, device="cuda")
+    mask = torch.from_numpy(synth.grpo_token_case(with_logits=False).mask).cuda()
+    w = torch.empty(mask.numel(), device="cuda")
+    f_adv = lambda: chk(L.grpo_group_advantages(P(rewards), 4, 4, 1e-4, 1, P(adv), s))
+    f_w = lambda: chk(L.grpo_loss_weights(P(mask), 4, 512, 0, P(w), s))
+    for f in (f_adv, f_w):
+        f()
+    t_adv, t_w = kernel_times([[f_adv, f_w]], 200, torch)
+    res = base_line(args, "entropy backward GB/s at 65536x32000 bf16", gbs, "GB/s", ms,
+                    {"workload": "entropy_from_logits_bwd, N=65536 V=32000 bf16, N(0,3^2) + 8 "
+                                 "peak, upstream grad N(0,1) (no zero rows), T=1",
+                     "rows": N, "V": V})
+    res.update({
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "kernels": {"entropy_bwd": {"ms": round(kt, 4), "bytes": nbytes, "GB/s": round(kgbs, 1)},
+                    "group_advantages_B4_G4": {"us": round(t_adv * 1e3, 2)},
+                    "loss_weights_token_B4_L512": {"us": round(t_w * 1e3, 2)}},
+        "roofline": {"kernel": "entropy_bwd", "bound": "hbm", "achieved": round(kgbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("entropy_bwd", "entropy-bwd")},
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        R = 512
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            zz = oracle.decode_bf16(case.logits[:R])
+            oracle.entropy_from_logits_bwd(zz, case.grad[:R])
+            reps += 1
+            if time.perf_counter() - t0 > 10.0 or reps >= 30:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": R * V * 4 / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} x {R} rows of the entropy backward in float64 "
+                                         f"NumPy (computing lse and H itself), {dt:.3f} s each, "
+                                         f"single thread; host CPU {cpu_model()}"}
+    return res
+
+
+# ---------------------------------------------------------------------------
 # chunked fused-linear
 # ---------------------------------------------------------------------------
 def run_fused(args, torch, grl, synth):
@@ -489,6 +570,8 @@ def main():
         res = run_grpo(args, torch, grl, synth, "sequence")
     elif args.workload == "rows":
         res = run_rows(args, torch, grl, synth)
+    elif args.workload == "entropy-bwd":
+        res = run_entropy_bwd(args, torch, grl, synth)
     else:
         res = run_fused(args, torch, grl, synth)
     print(json.dumps(res), flush=True)

@@ -274,6 +274,57 @@ int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const void* B, int 
                    int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                    int accumulate, void* stream);
 
+/* ------------------------------------------------------------------------
+ * entropy_from_logits_bwd -- backward of the per-row entropy
+ * H = -sum_j p_j log p_j, p = softmax(z / T) [AXOLOTL part 1 defines H; the
+ * pages give it no backward, so this is its derivative]:
+ *   dlogits_j = -grad_entropy[r] / T * p_j * (log p_j + H[r]),
+ *   log p_j = z_j / T - lse[r],
+ * for entropy-regularised losses.  Rows with grad_entropy == 0 take the
+ * all-zero, write-only path (no logits read).
+ * logits [rows, ld] (in); lse, entropy fp32 [rows] (in: the forward's, at the
+ * same T -- grpo_logits_fwd writes both); grad_entropy fp32 [rows] (in);
+ * dlogits [rows, ld_out] of `dtype` (out; may alias logits if ld_out == ld).
+ * Errors as for selective_log_softmax_bwd.
+ * ------------------------------------------------------------------------ */
+int entropy_from_logits_bwd(const void* logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                            float temperature, const float* lse, const float* entropy,
+                            const float* grad_entropy, void* dlogits, int64_t ld_out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * grpo_group_advantages -- group-relative advantages of n rewards in
+ * consecutive groups of group_size (the completions of one prompt):
+ *   A = (r - mean_group) / (sample_std_group + eps)   (scale = 1),
+ *   A =  r - mean_group                                (scale = 0).
+ * The pages name zero-advantage sequences [LIGER-BWD summary] but give no
+ * formula; this is the plain reading of "group-relative", with the sample
+ * (n - 1) standard deviation.  A group whose rewards are all equal (or a
+ * group of one) gets exactly 0 -- the rows the zero-gradient path skips.
+ * Sums are taken in fp64; a NaN reward makes its group NaN.
+ * rewards, adv fp32 [n] (in, out).  n % group_size == 0 (else
+ * GRPO_ERR_SHAPE); eps >= 0 and scale in {0, 1} (else GRPO_ERR_PARAM).
+ * ------------------------------------------------------------------------ */
+int grpo_group_advantages(const float* rewards, int64_t n, int64_t group_size, float eps,
+                          int scale, float* adv, void* stream);
+
+/* Reductions of the per-token losses for grpo_loss_weights. */
+enum { GRPO_REDUCE_TOKEN = 0, GRPO_REDUCE_SEQUENCE = 1, GRPO_REDUCE_CONSTANT = 2 };
+
+/* ------------------------------------------------------------------------
+ * grpo_loss_weights -- the per-token weights dloss = dLoss/dloss_bt that the
+ * backward entry points take [LIGER-BWD "Code analysis": the backward scales
+ * by dloss], for three reductions of the per-token losses l (m = mask, all
+ * ones when mask is NULL; the pages do not fix the reduction):
+ *   GRPO_REDUCE_TOKEN     Loss = sum m l / max(sum m, 1)
+ *   GRPO_REDUCE_SEQUENCE  Loss = (1/B) sum_b sum_t m l / max(n_b, 1)
+ *   GRPO_REDUCE_CONSTANT  Loss = sum m l / (B L)
+ * Counts are exact integers; each weight is the correctly rounded fp32 of
+ * its reciprocal.  mask uint8 [B*L] or NULL (in); dloss fp32 [B*L] (out).
+ * ------------------------------------------------------------------------ */
+int grpo_loss_weights(const uint8_t* mask, int64_t B, int64_t L, int reduction, float* dloss,
+                      void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* grpo_status_string(int status);
 

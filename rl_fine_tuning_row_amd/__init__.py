@@ -10,4 +10,5 @@ from ._lib import (  # noqa: F401
     fused_linear_grpo_workspace_bytes, grpo_gemm_bf16, grpo_logits_bwd, grpo_logits_fwd,
     grpo_logits_fwd_bwd, header_functions,
     lib, selective_log_softmax, selective_log_softmax_bwd,
+    entropy_from_logits_bwd, grpo_group_advantages, grpo_loss_weights, GRPO_REDUCE,
 )

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "grpo_rows.h")
 GRPO_F32, GRPO_BF16 = 0, 1
 GRPO_TOKEN, GRPO_SEQUENCE = 0, 1
 GRPO_FLAG_FORCE_DENSE = 1
+GRPO_REDUCE = {"token": 0, "sequence": 1, "constant": 2}
 STATUS = {0: "GRPO_OK", 1: "GRPO_ERR_NULL", 2: "GRPO_ERR_SHAPE", 3: "GRPO_ERR_STRIDE",
           4: "GRPO_ERR_DTYPE", 5: "GRPO_ERR_ALIGN", 6: "GRPO_ERR_WORKSPACE",
           7: "GRPO_ERR_LAUNCH", 8: "GRPO_ERR_PARAM"}
@@ -60,6 +61,9 @@ _SIGS = {
     "fused_linear_grpo_workspace_bytes": [_I64, _I64, _I64],
     "grpo_gemm_bf16": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I64, _I64, _I64, _I, _P],
     "grpo_status_string": [_I],
+    "entropy_from_logits_bwd": [_P, _I, _I64, _I64, _I64, _F, _P, _P, _P, _P, _I64, _P],
+    "grpo_group_advantages": [_P, _I64, _I64, _F, _I, _P, _P],
+    "grpo_loss_weights": [_P, _I64, _I64, _I, _P, _P],
 }
 _RESTYPE = {"fused_linear_grpo_workspace_bytes": ctypes.c_size_t,
             "grpo_status_string": ctypes.c_char_p}
@@ -335,6 +339,54 @@ def selective_log_softmax_bwd(logits, ids, lse, grad_logp, temperature=1.0, dlog
                                          _stream(stream))
     _check("selective_log_softmax_bwd", st)
     return dlogits
+
+
+def entropy_from_logits_bwd(logits, lse, entropy, grad_entropy, temperature=1.0, dlogits=None,
+                            stream=None):
+    """dlogits of sum_r grad_entropy[r] * H[r]; lse and entropy from the forward."""
+    rows, V, ld = _rows_view(logits)
+    _need(lse, torch.float32, rows, "lse")
+    _need(entropy, torch.float32, rows, "entropy")
+    _need(grad_entropy, torch.float32, rows, "grad_entropy")
+    if dlogits is None:
+        dlogits = torch.empty((rows, V), dtype=logits.dtype, device=logits.device)
+    r2, v2, ld_out = _rows_view(dlogits)
+    if (r2, v2) != (rows, V) or dlogits.dtype != logits.dtype:
+        raise ValueError("dlogits must be [rows, V] of the logits' dtype")
+    st = lib().entropy_from_logits_bwd(_ptr(logits), _dtype_code(logits), rows, V, ld,
+                                       float(temperature), _ptr(lse), _ptr(entropy),
+                                       _ptr(grad_entropy), _ptr(dlogits), ld_out, _stream(stream))
+    _check("entropy_from_logits_bwd", st)
+    return dlogits
+
+
+def grpo_group_advantages(rewards, group_size, eps=1e-4, scale=True, adv=None, stream=None):
+    """Group-relative advantages of consecutive groups of `group_size` rewards."""
+    if not rewards.is_cuda:
+        raise ValueError("rewards must be a device tensor")
+    n = rewards.numel()
+    _need(rewards, torch.float32, n, "rewards")
+    if adv is None:
+        adv = torch.empty_like(rewards)
+    _need(adv, torch.float32, n, "adv")
+    st = lib().grpo_group_advantages(_ptr(rewards), n, int(group_size), float(eps),
+                                     1 if scale else 0, _ptr(adv), _stream(stream))
+    _check("grpo_group_advantages", st)
+    return adv
+
+
+def grpo_loss_weights(mask, B, L, reduction="token", dloss=None, device=None, stream=None):
+    """Per-token weights dloss of a reduction ("token", "sequence", "constant")."""
+    if mask is not None:
+        _need(mask, torch.uint8, B * L, "mask")
+        device = mask.device
+    if dloss is None:
+        dloss = torch.empty(B * L, dtype=torch.float32, device=device or "cuda")
+    _need(dloss, torch.float32, B * L, "dloss")
+    st = lib().grpo_loss_weights(_ptr(mask), int(B), int(L), GRPO_REDUCE[reduction],
+                                 _ptr(dloss), _stream(stream))
+    _check("grpo_loss_weights", st)
+    return dloss
 
 
 def fused_linear_grpo_workspace_bytes(rows: int, V: int, H: int) -> int:

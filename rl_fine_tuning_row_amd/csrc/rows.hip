@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void seq_fwd_epilogue_kernel(SeqArgs a) {
 // ---------------------------------------------------------------------------
 template <typename TIn, int WG>
 __device__ __forceinline__ float row_dlogp(const BwdArgs& a, int64_t r) {
-  if (a.mode == BWD_LSM) return a.dloss[r];
+  if (a.mode == BWD_LSM || a.mode == BWD_ENTROPY) return a.dloss[r];
   const float logp = a.logp[r];
   const float w = a.dloss[r];
   float klg = 0.0f;
@@ -203,13 +203,14 @@ __device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float va
   }
 }
 
-template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC, bool NTL>
+// ENT: the entropy backward, dz_j = -(g/T) p_j (log p_j + H), no sampled id
+template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC, bool NTL, bool ENT = false>
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   const int64_t r = blockIdx.x;
   if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const float g = uniform(row_dlogp<TIn, WG>(a, r));
-  const int64_t y = a.ids[r];
-  const bool valid = y >= 0 && y < a.V;
+  const int64_t y = ENT ? 0 : a.ids[r];
+  const bool valid = ENT || (y >= 0 && y < a.V);
   TOut* __restrict__ out = static_cast<TOut*>(a.dlogits) + r * a.ld_out;
   const bool zero = (g == 0.0f);
   if (threadIdx.x == 0 && a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
@@ -222,10 +223,17 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
     return;
   }
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
-  const float coef = g / a.T;
+  const float coef = ENT ? -g / a.T : g / a.T;
   const float lse2 = a.lse[r] * kLog2e;
   const float c = a.c;
+  const float Hr = ENT ? a.entropy[r] : 0.0f;
   const int yi = int(y);
+  // one element of the dense path: u = log2 p
+  auto grad_elem = [&](float x) {
+    const float u = fmaf(x, c, -lse2);
+    if constexpr (ENT) return coef * exp2_fast(u) * fmaf(u, kLn2, Hr);
+    else return -coef * exp2_fast(u);
+  };
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
     const u32x4* rv = reinterpret_cast<const u32x4*>(row);
@@ -241,8 +249,8 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
         float x[VE];
         Vec<TIn>::unpack(v[u], x);
 #pragma unroll
-        for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
-        if (i + u * WG == vy) {
+        for (int k = 0; k < VE; ++k) x[k] = grad_elem(x[k]);
+        if (!ENT && i + u * WG == vy) {
 #pragma unroll
           for (int k = 0; k < VE; ++k)
             if (k == ky) x[k] += coef;
@@ -254,8 +262,8 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
       float x[VE];
       Vec<TIn>::unpack(load16<NTL>(rv + i), x);
 #pragma unroll
-      for (int k = 0; k < VE; ++k) x[k] = -coef * exp2_fast(fmaf(x[k], c, -lse2));
-      if (i == vy) {
+      for (int k = 0; k < VE; ++k) x[k] = grad_elem(x[k]);
+      if (!ENT && i == vy) {
 #pragma unroll
         for (int k = 0; k < VE; ++k)
           if (k == ky) x[k] += coef;
@@ -264,14 +272,14 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
     }
     const int j = nvec * VE + threadIdx.x;
     if (j < a.V) {
-      float d = -coef * exp2_fast(fmaf(load_elem(row + j), c, -lse2));
-      if (j == yi) d += coef;
+      float d = grad_elem(load_elem(row + j));
+      if (!ENT && j == yi) d += coef;
       store_elem(out + j, d);
     }
   } else {
     for (int j = threadIdx.x; j < a.V; j += WG) {
-      float d = -coef * exp2_fast(fmaf(load_elem(row + j), c, -lse2));
-      if (j == yi) d += coef;
+      float d = grad_elem(load_elem(row + j));
+      if (!ENT && j == yi) d += coef;
       store_elem(out + j, d);
     }
   }
@@ -642,6 +650,26 @@ int launch_fused(const FusedArgs& a, int dtype, int64_t rows, bool need_t, bool&
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
+int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
+  const int es = elem_size(dtype);
+  const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
+  const bool small = a.V * int64_t(es) / 16 <= 1024;  // the backward's shape rule
+#define ENT_LAUNCH(T, W, VEC_)                                                              \
+  hipLaunchKernelGGL((row_bwd_kernel<T, T, W, (VEC_ ? 2 : 4), VEC_, false, true>),         \
+                     dim3(unsigned(rows)), dim3(W), 0, s, a)
+  if (dtype == GRPO_BF16) {
+    if (!vec) ENT_LAUNCH(uint16_t, 256, false);
+    else if (small) ENT_LAUNCH(uint16_t, 256, true);
+    else ENT_LAUNCH(uint16_t, 1024, true);
+  } else {
+    if (!vec) ENT_LAUNCH(float, 256, false);
+    else if (small) ENT_LAUNCH(float, 256, true);
+    else ENT_LAUNCH(float, 1024, true);
+  }
+#undef ENT_LAUNCH
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
 int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s) {
   const Shape sh = pick_bwd_shape(rows, a.V, 4);
   // fp32 rows in 16-byte vectors, bf16 rows in 8-byte vectors
@@ -910,6 +938,38 @@ extern "C" int selective_log_softmax(const void* logits, int dtype, int64_t rows
   a.logp = logp;
   a.lse = lse;
   return launch_fwd(a, dtype, rows, false, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int entropy_from_logits_bwd(const void* logits, int dtype, int64_t rows, int64_t V,
+                                       int64_t ld, float temperature, const float* lse,
+                                       const float* entropy, const float* grad_entropy,
+                                       void* dlogits, int64_t ld_out, void* stream) {
+  int st = check_matrix(logits, dtype, rows, V, ld);
+  if (st != GRPO_OK) return st;
+  if (check_temperature(temperature) != GRPO_OK) return GRPO_ERR_PARAM;
+  if (ld_out < V) return GRPO_ERR_STRIDE;
+  if (dlogits == logits && ld_out != ld) return GRPO_ERR_STRIDE;
+  if (rows > 0 &&
+      (lse == nullptr || entropy == nullptr || grad_entropy == nullptr || dlogits == nullptr))
+    return GRPO_ERR_NULL;
+  if (!aligned(lse, 4) || !aligned(entropy, 4) || !aligned(grad_entropy, 4) ||
+      !aligned(dlogits, elem_size(dtype)))
+    return GRPO_ERR_ALIGN;
+  if (rows == 0) return GRPO_OK;
+  BwdArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.dlogits = dlogits;
+  a.ld_out = ld_out;
+  a.V = int32_t(V);
+  a.L = 1;
+  a.lse = lse;
+  a.entropy = entropy;
+  a.dloss = grad_entropy;
+  a.T = temperature;
+  a.c = kLog2e / temperature;
+  a.mode = BWD_ENTROPY;
+  return launch_bwd_entropy(a, dtype, rows, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64_t V,

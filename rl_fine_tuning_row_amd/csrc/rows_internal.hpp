@@ -8,7 +8,7 @@
 namespace grpo {
 
 enum FwdMode : int32_t { FWD_GRPO = 0, FWD_ENTROPY = 1, FWD_LSM = 2 };
-enum BwdMode : int32_t { BWD_GRPO = 0, BWD_LSM = 1 };
+enum BwdMode : int32_t { BWD_GRPO = 0, BWD_LSM = 1, BWD_ENTROPY = 2 };
 
 struct FwdArgs {
   const void* logits;
@@ -47,7 +47,8 @@ struct BwdArgs {
   const float* logp;
   const float* lse;
   const float* seq_ratio;
-  const float* dloss;  // grad_logp in BWD_LSM mode
+  const float* dloss;    // grad_logp in BWD_LSM mode, grad_entropy in BWD_ENTROPY
+  const float* entropy;  // BWD_ENTROPY: the rows' entropies H
   float T, c, beta, lo, hi;
   int32_t mode, level, force_dense;
   uint8_t* zero_row;
@@ -73,5 +74,7 @@ int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream
 int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s);
 // Backward row kernel over fp32 logits writing bf16 dlogits.
 int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s);
+// Entropy backward (BWD_ENTROPY) on logits and dlogits of the same dtype.
+int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s);
 
 }  // namespace grpo

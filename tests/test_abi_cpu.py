@@ -108,3 +108,36 @@ def test_fused_workspace_query(L):
     assert L.fused_linear_grpo_workspace_bytes(0, 100, 64) >= 0
     assert L.fused_linear_grpo_workspace_bytes(1024, 151936, 1024) > 1024 * 151936 * 4
     assert L.fused_linear_grpo_workspace_bytes(-1, 100, 64) == 0
+
+
+def test_entropy_bwd_validation(L):
+    b = L.entropy_from_logits_bwd
+    assert b(FAKE, 1, 10, 100, 100, 1.0, None, FAKE, FAKE, FAKE, 100, None) == NULL
+    assert b(FAKE, 1, 10, 100, 100, 1.0, FAKE, None, FAKE, FAKE, 100, None) == NULL
+    assert b(FAKE, 1, 10, 100, 100, 1.0, FAKE, FAKE, None, FAKE, 100, None) == NULL
+    assert b(FAKE, 1, 10, 100, 100, 1.0, FAKE, FAKE, FAKE, FAKE, 99, None) == STRIDE
+    assert b(FAKE, 1, 10, 100, 100, 0.0, FAKE, FAKE, FAKE, FAKE, 100, None) == PARAM
+    assert b(FAKE, 1, 10, 100, 100, 1.0, FAKE_ODD, FAKE, FAKE, FAKE, 100, None) == ALIGN
+    assert b(FAKE, 1, 0, 100, 100, 1.0, None, None, None, None, 100, None) == OK
+
+
+def test_group_advantages_validation(L):
+    g = L.grpo_group_advantages
+    assert g(FAKE, 10, 4, 1e-4, 1, FAKE, None) == SHAPE      # 10 % 4 != 0
+    assert g(FAKE, 8, 0, 1e-4, 1, FAKE, None) == SHAPE
+    assert g(FAKE, -4, 4, 1e-4, 1, FAKE, None) == SHAPE
+    assert g(FAKE, 8, 4, -1.0, 1, FAKE, None) == PARAM
+    assert g(FAKE, 8, 4, float("nan"), 1, FAKE, None) == PARAM
+    assert g(FAKE, 8, 4, 1e-4, 2, FAKE, None) == PARAM
+    assert g(None, 8, 4, 1e-4, 1, FAKE, None) == NULL
+    assert g(FAKE_ODD, 8, 4, 1e-4, 1, FAKE, None) == ALIGN
+    assert g(None, 0, 4, 1e-4, 1, None, None) == OK
+
+
+def test_loss_weights_validation(L):
+    w = L.grpo_loss_weights
+    assert w(None, 4, 8, 3, FAKE, None) == PARAM
+    assert w(None, -1, 8, 0, FAKE, None) == SHAPE
+    assert w(None, 4, 8, 0, None, None) == NULL
+    assert w(None, 4, 8, 0, FAKE_ODD, None) == ALIGN
+    assert w(None, 0, 8, 0, None, None) == OK
