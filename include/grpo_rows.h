@@ -47,6 +47,8 @@
  *    layouts take an element-wise path with the same results.
  *  - Aliasing: dlogits may alias logits only with the same dtype and
  *    ld_out == ld (in place).  No other output may alias an input.
+ *  - Limits: shapes whose launches would need more than 2^31 - 1
+ *    workgroups in one grid dimension return GRPO_ERR_SHAPE.
  *  - Thread safety: stateless and reentrant.  rows == 0 is a no-op.
  */
 #ifndef GRPO_ROWS_H

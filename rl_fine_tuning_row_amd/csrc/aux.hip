@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void weights_seq_kernel(const uint8_t* __restr
 extern "C" int grpo_group_advantages(const float* rewards, int64_t n, int64_t group_size,
                                      float eps, int scale, float* adv, void* stream) {
   if (n < 0 || group_size <= 0 || group_size > (int64_t(1) << 24) || n % group_size != 0 ||
-      n > (int64_t(1) << 40))
+      n > (int64_t(1) << 31))
     return GRPO_ERR_SHAPE;
   if (!(eps >= 0.0f) || (scale != 0 && scale != 1)) return GRPO_ERR_PARAM;
   if (n == 0) return GRPO_OK;

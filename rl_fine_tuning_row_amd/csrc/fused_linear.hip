@@ -198,6 +198,16 @@ int check_fused(const void* hidden, int64_t nseq, int64_t L, int64_t H, const vo
   if (nseq < 0 || L <= 0 || H <= 0 || V <= 0) return GRPO_ERR_SHAPE;
   if (H % 64 != 0 || H > 65536 || V % 8 != 0 || V > (int64_t(1) << 30)) return GRPO_ERR_SHAPE;
   if (nseq > (int64_t(1) << 30) / L) return GRPO_ERR_SHAPE;
+  {
+    // launch sizes: the grad_hidden scatter grid (R H / 1024) and the products'
+    // tile counts (128 x 128 tiles, K-splits included) must fit a 31-bit grid
+    const int64_t R = nseq * L;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (R * H / 1024 > lim) return GRPO_ERR_SHAPE;
+    if (((R + 127) / 128) * ((V + 127) / 128) > lim) return GRPO_ERR_SHAPE;
+    if (((V + 127) / 128) * ((H + 127) / 128) > lim) return GRPO_ERR_SHAPE;
+    if (((R + 127) / 128) * ((H + 127) / 128) * 16 > lim) return GRPO_ERR_SHAPE;
+  }
   const int st = check_params(p);
   if (st != GRPO_OK) return st;
   if (p->level != GRPO_TOKEN || (p->flags & GRPO_FLAG_FORCE_DENSE)) return GRPO_ERR_PARAM;

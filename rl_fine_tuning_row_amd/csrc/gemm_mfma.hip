@@ -712,6 +712,8 @@ extern "C" int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const vo
                               int64_t N, int64_t K, int accumulate, void* stream) {
   if (M < 0 || N < 0 || K < 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return GRPO_ERR_SHAPE;
+  // the grid (128 x 128 tiles at most) must fit 31 bits
+  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
   if (M == 0 || N == 0) return GRPO_OK;
   if (A == nullptr || B == nullptr || C == nullptr) return GRPO_ERR_NULL;
   if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1) ||

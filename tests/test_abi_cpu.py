@@ -141,3 +141,16 @@ def test_loss_weights_validation(L):
     assert w(None, 4, 8, 0, None, None) == NULL
     assert w(None, 4, 8, 0, FAKE_ODD, None) == ALIGN
     assert w(None, 0, 8, 0, None, None) == OK
+
+
+def test_launch_size_limits(L):
+    """Shapes whose grids would overflow 31 bits are rejected before any launch."""
+    g = L.grpo_gemm_bf16
+    assert g(FAKE, 0, 1 << 30, FAKE, 0, 1 << 30, FAKE, 1 << 30, 1 << 30, 1 << 30, 8, 0, None) == SHAPE
+    f = L.fused_linear_grpo_chunk
+    p = GrpoParams(1.0, 0.0, 0.2, 0.2, 0, 0)
+    # R = 2^20 rows, H = 65536: R H / 1024 = 2^26 fits; V = 2^30 makes the logits grid too big
+    assert f(FAKE, 1 << 10, 1 << 10, 65536, FAKE, 1 << 30, FAKE, FAKE, None, FAKE, None, FAKE,
+             ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 62, None) == SHAPE
+    a = L.grpo_group_advantages
+    assert a(FAKE, (1 << 31) + 4, 4, 1e-4, 1, FAKE, None) == SHAPE
