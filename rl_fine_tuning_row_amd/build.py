@@ -86,7 +86,28 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    build_c_check(hipcc, verbose)
     return LIB_PATH
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c", "abi_check.cpp")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c", "abi_check")
+
+
+def build_c_check(hipcc: str, verbose: bool = False) -> None:
+    """Compile tests/c/abi_check.cpp, a C++ program that uses the library
+    through the C ABI alone (linked against libgrpo_rows.so, found through a
+    relative rpath)."""
+    if not os.path.exists(C_CHECK_SRC):
+        return
+    cmd = [hipcc, *COMMON, "-I", INCLUDE, C_CHECK_SRC, "-L", PKG, "-lgrpo_rows",
+           "-Wl,-rpath,$ORIGIN/../../rl_fine_tuning_row_amd", "-o", C_CHECK_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {C_CHECK_SRC}:\n{errs}")
 
 
 if __name__ == "__main__":
