@@ -83,6 +83,22 @@ def test_single_pass_shapes(dtype, V, ld_extra):
     path inside the same call; ragged tails take the single pass."""
     lib = require_gpu()
     say(f"single-pass shapes: {dtype} V={V} ld=V+{ld_extra}")
+    _edge_case(lib, dtype, V, ld_extra, 0.9)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 40), ("bf16", 1003), ("f32", 17), ("f32", 200)])
+@pytest.mark.parametrize("T", [0.3, 0.5, 0.7, 1.0, 1.3, 2.0])
+def test_single_pass_lanes_without_elements(dtype, V, T):
+    """Rows shorter than the workgroup leave lanes with no element.  Such a lane
+    once folded its fill values into garbage sums (the rounding error of
+    fill * log2e / T, positive for some temperatures -> inf -> NaN after the
+    merge); it must contribute nothing at every temperature."""
+    lib = require_gpu()
+    say(f"single-pass short rows: {dtype} V={V} T={T}")
+    _edge_case(lib, dtype, V, 0, T)
+
+
+def _edge_case(lib, dtype, V, ld_extra, T):
     B, L = 2, 3
     rng = np.random.default_rng(V)
     zf = (rng.standard_normal((B * L, V + ld_extra)) * 2.0).astype(np.float32)
@@ -90,12 +106,12 @@ def test_single_pass_shapes(dtype, V, ld_extra):
     t = logits_to_dev(zb, dtype)[:, :V]
     z64 = oracle.to_f64(zb, dtype)[:, :V]
     ids = rng.integers(0, V, B * L).astype(np.int64)
-    lp, _ = oracle.selective_log_softmax(z64, ids, 0.9)
+    lp, _ = oracle.selective_log_softmax(z64, ids, T)
     case = synth.GrpoCase(name="edge", B=B, L=L, V=V, dtype=dtype, logits=None, ids=ids,
                           adv=np.array([0.7, -1.1], np.float32), mask=np.ones(B * L, np.uint8),
                           old_noise=rng.standard_normal(B * L) * 0.2,
                           ref_noise=rng.standard_normal(B * L) * 0.1,
-                          dloss=np.ones(B * L, np.float32), temperature=0.9, beta=0.04,
+                          dloss=np.ones(B * L, np.float32), temperature=T, beta=0.04,
                           eps_low=0.2, eps_high=0.28, level="token")
     inp = GrpoInputs(case, lp)
     o, dz, zr = run_single_pass(lib, t, inp)
