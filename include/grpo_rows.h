@@ -116,7 +116,8 @@ typedef struct grpo_params {
  * ref_logp   fp32 [B*L] or NULL: NULL means no reference model (ref equals
  *            the policy, kl = 0)             (in)
  * adv        fp32 [B] advantage per sequence (in)
- * mask       uint8 [B*L] completion mask or NULL (all ones); used only at
+ * mask       uint8 [B*L] completion mask or NULL (all ones; a nonzero entry
+ *            counts as 1); used only at
  *            GRPO_SEQUENCE (per-token losses are reported for every token;
  *            the caller's reduction applies the mask)  (in)
  * loss, logp, lse  fp32 [B*L]                (out, required)

@@ -125,6 +125,14 @@ def k3(d: np.ndarray) -> np.ndarray:
     return np.expm1(d) - d
 
 
+def _mask01(mask, n: int) -> np.ndarray:
+    """Completion mask as float64 0/1: a nonzero entry is a kept token (the
+    mask of a completion is 1 up to its length, 0 after it); None = all kept."""
+    if mask is None:
+        return np.ones(n)
+    return (np.asarray(mask).reshape(-1) != 0).astype(np.float64)
+
+
 def _advantage_per_row(adv, B, L):
     return np.repeat(np.asarray(adv, dtype=np.float64), L)
 
@@ -149,7 +157,7 @@ def grpo_forward(z, ids, old_logp, ref_logp, adv, mask, B, L, temperature, beta,
     logp, lse = selective_log_softmax(z, ids, temperature)
     H = entropy_from_logits(z, temperature)
     old = np.asarray(old_logp, dtype=np.float64)
-    m = np.ones(N) if mask is None else np.asarray(mask, dtype=np.float64)
+    m = _mask01(mask, N)
     if ref_logp is None:
         d = np.zeros(N)
     else:
@@ -186,7 +194,7 @@ def grpo_dlogp(fwd: dict, ref_logp, adv, mask, dloss, B, L, beta, level="token")
     N = B * L
     logp = fwd["logp"]
     w = np.asarray(dloss, dtype=np.float64)
-    m = np.ones(N) if mask is None else np.asarray(mask, dtype=np.float64)
+    m = _mask01(mask, N)
     if ref_logp is None or beta == 0.0:
         kl_grad = np.zeros(N)
     else:
@@ -234,7 +242,7 @@ def grpo_backward(z, ids, old_logp, ref_logp, adv, mask, dloss, B, L, temperatur
 
 def token_mean_loss(loss: np.ndarray, mask) -> float:
     """Caller-side token-mean reduction: sum m * loss / max(sum m, 1)."""
-    m = np.ones_like(loss) if mask is None else np.asarray(mask, dtype=np.float64)
+    m = _mask01(mask, loss.size)
     return float((m * loss).sum() / max(m.sum(), 1.0))
 
 
@@ -340,7 +348,7 @@ def loss_weights(mask, B: int, L: int, reduction: str) -> np.ndarray:
     Readings: "token"     L = sum m l / max(sum m, 1)       (the harness's),
               "sequence"  L = (1/B) sum_b sum_t m l / max(n_b, 1),
               "constant"  L = sum m l / (B L)."""
-    m = (np.ones(B * L) if mask is None else np.asarray(mask, dtype=np.float64)).reshape(B, L)
+    m = _mask01(mask, B * L).reshape(B, L)
     if reduction == "token":
         w = m / max(m.sum(), 1.0)
     elif reduction == "sequence":

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void seq_fwd_epilogue_kernel(SeqArgs a) {
   const int64_t base = b * a.L;
   float sx = 0.0f, sm = 0.0f;
   for (int t = threadIdx.x; t < a.L; t += 256) {
-    const float m = a.mask != nullptr ? float(a.mask[base + t]) : 1.0f;
+    const float m = a.mask != nullptr ? float(a.mask[base + t] != 0) : 1.0f;
     sx += m * (a.logp[base + t] - a.old_logp[base + t]);
     sm += m;
   }
@@ -162,7 +162,7 @@ __device__ __forceinline__ float row_dlogp(const BwdArgs& a, int64_t r) {
   float ws = 0.0f, ms = 0.0f;
   for (int t = threadIdx.x; t < a.L; t += WG) {
     ws += a.dloss[base + t];
-    ms += a.mask != nullptr ? float(a.mask[base + t]) : 1.0f;
+    ms += a.mask != nullptr ? float(a.mask[base + t] != 0) : 1.0f;
   }
   __shared__ float sh[2 * (WG / 64)];
   block_sum2<WG>(ws, ms, sh);
@@ -172,7 +172,7 @@ __device__ __forceinline__ float row_dlogp(const BwdArgs& a, int64_t r) {
   const float cr = ratio < a.lo ? a.lo : (ratio > a.hi ? a.hi : ratio);
   const bool clipped = cr * A < ratio * A;
   const float coef = clipped ? 0.0f : -ratio * A;
-  const float m = a.mask != nullptr ? float(a.mask[r]) : 1.0f;
+  const float m = a.mask != nullptr ? float(a.mask[r] != 0) : 1.0f;
   return coef * ws * m / n + klg * w;
 }
 

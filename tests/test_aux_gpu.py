@@ -199,3 +199,27 @@ def test_rewards_to_logits_chain():
     assert np.array_equal(zero, zero_o.astype(bool))
     assert zero[:4 * c.L].all()          # the all-equal group
     assert (bits(dz)[zero] == 0).all()
+
+
+def test_mask_entries_are_boolean():
+    """Nonzero mask entries count as 1: a 0/2 mask gives bit-identical
+    sequence-level forward and backward and loss weights."""
+    lib = require_gpu()
+    c = synth.grpo_sequence_case(with_logits=False, B=4, L=64, V=2048)
+    say("mask 0/2 == mask 0/1: sequence level B4 L64 V2048, weights")
+    rng = np.random.default_rng(51)
+    zb = synth.f32_to_bf16_bits((rng.standard_normal((c.N, c.V)) * 2).astype(np.float32))
+    z = logits_to_dev(zb, "bf16")
+    mask = (rng.random(c.N) < 0.8).astype(np.uint8)
+    old = (rng.standard_normal(c.N) * 0.3 - 7.0).astype(np.float32)
+    kw = dict(temperature=1.0, beta=0.0, eps_low=0.2, eps_high=0.28, level="sequence")
+    res = []
+    for m in (mask, mask * 2):
+        w = lib.grpo_loss_weights(dev(m), c.B, c.L, "sequence")
+        fwd = lib.grpo_logits_fwd(z, dev(c.ids), dev(old), dev(c.adv), c.B, c.L, mask=dev(m), **kw)
+        dz, zr = lib.grpo_logits_bwd(z, dev(c.ids), dev(old), dev(c.adv), c.B, c.L, fwd["logp"],
+                                     fwd["lse"], w, mask=dev(m), seq_ratio=fwd["seq_ratio"], **kw)
+        torch.cuda.synchronize()
+        res.append((bits(w), bits(fwd["loss"]), bits(fwd["seq_ratio"]), bits(dz), zr.cpu().numpy()))
+    for x, y in zip(*res):
+        assert np.array_equal(x, y)

@@ -126,3 +126,24 @@ def test_loss_weights_closed_sums():
     np.testing.assert_allclose(ws, [0.25, 0.0, 0.25, 0.25], atol=1e-15)
     assert (oracle.loss_weights(None, B, L, "constant") == 1.0 / (B * L)).all()
     assert (oracle.loss_weights(np.zeros(B * L), B, L, "token") == 0.0).all()
+
+
+def test_mask_entries_are_boolean():
+    """A completion mask's nonzero entries count as 1 (a 0/2 mask is the 0/1 mask)."""
+    rng = np.random.default_rng(15)
+    B, L = 3, 7
+    mask = (rng.random(B * L) < 0.7).astype(np.uint8)
+    for red in ("token", "sequence", "constant"):
+        np.testing.assert_array_equal(oracle.loss_weights(mask * 2, B, L, red),
+                                      oracle.loss_weights(mask, B, L, red))
+    z = rng.standard_normal((B * L, 11))
+    ids = rng.integers(0, 11, B * L)
+    lp, _ = oracle.selective_log_softmax(z, ids)
+    old = lp + rng.standard_normal(B * L) * 0.3
+    adv = rng.standard_normal(B)
+    args = dict(z=z, ids=ids, old_logp=old, ref_logp=None, adv=adv, B=B, L=L, temperature=1.0,
+                beta=0.0, eps_low=0.2, eps_high=0.2, level="sequence")
+    a = oracle.grpo_forward(mask=mask, **args)
+    b = oracle.grpo_forward(mask=mask * 2, **args)
+    for k in ("loss", "seq_ratio"):
+        np.testing.assert_array_equal(a[k], b[k])
