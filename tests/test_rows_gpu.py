@@ -396,3 +396,36 @@ def test_nan_logits_propagate():
     lp, lse = lib.selective_log_softmax(t, dev(np.array([0, 1, 2, 3], np.int64)))
     assert np.isnan(H[1]) and np.isnan(lse.cpu().numpy()[1])
     assert np.isfinite(np.delete(H, 1)).all()
+
+
+@pytest.mark.parametrize("with_ref", [False, True])
+def test_sequence_level_partial_masks(with_ref):
+    """Sequence level with completion masks of lengths 12, 0, 1 and 7 (an
+    empty sequence, a one-token sequence): the mask-weighted mean log-ratio,
+    its clip and the spread gradient against the oracle; every row."""
+    lib = require_gpu()
+    say(f"sequence level with partial masks (lengths 12, 0, 1, 7), ref={'noise' if with_ref else 'none'}")
+    B, L, V = 4, 12, 300
+    rng = np.random.default_rng(61)
+    z = (rng.standard_normal((B * L, V)) * 2.0).astype(np.float32)
+    z64 = z.astype(np.float64)
+    ids = rng.integers(0, V, B * L).astype(np.int64)
+    T = 0.8
+    lp, _ = oracle.selective_log_softmax(z64, ids, T)
+    lengths = np.array([12, 0, 1, 7])
+    mask = (np.arange(L)[None, :] < lengths[:, None]).astype(np.uint8).reshape(-1)
+    case = synth.GrpoCase(name="seq-masks", B=B, L=L, V=V, dtype="f32", logits=z, ids=ids,
+                          adv=np.array([0.9, -0.4, 1.3, -1.0], np.float32), mask=mask,
+                          old_noise=np.repeat(rng.standard_normal(B) * 0.4, L),
+                          ref_noise=rng.standard_normal(B * L) * 0.1 if with_ref else None,
+                          dloss=mask.astype(np.float32), temperature=T, beta=0.04,
+                          eps_low=0.2, eps_high=0.28, level="sequence")
+    inp = GrpoInputs(case, lp)
+    fwd, dz, zr = run_grpo_gpu(lib, logits_to_dev(z, "f32"), inp)
+    o, g = oracle_expectations(inp, z64, fwd)
+    check_forward(case, o, fwd)
+    check_backward(case, o, g, dz, zr, z64, inp)
+    # the empty sequence (and the masked tail of the others) carries no
+    # policy gradient; without a reference model its rows are exactly zero
+    if not with_ref:
+        assert zr.cpu().numpy()[mask == 0].all()
