@@ -41,7 +41,8 @@
  *    GRPO_ERR_LAUNCH.  Data errors are not status codes (that would need a
  *    sync): an id outside [0, V) makes that row's outputs NaN and, where an
  *    err_count pointer is given, adds 1 to it with a device atomic.
- *    NaN/Inf in the logits propagate to the outputs of their row.
+ *    NaN/Inf in the logits propagate to the outputs of their row; finite
+ *    logits must lie above -1e30 (the normaliser's starting value).
  *  - Alignment: pointers must be aligned to their element size.  Rows whose
  *    byte address is 16-byte aligned take 128-bit loads and stores; other
  *    layouts take an element-wise path with the same results.

@@ -47,8 +47,6 @@ inline int check_params(const grpo_params* p) {
   return GRPO_OK;
 }
 
-inline int check_aligned4(const void* p) { return aligned(p, 4) ? GRPO_OK : GRPO_ERR_ALIGN; }
-
 // optional launch shape overrides "WG,UNROLL" for tuning sweeps:
 // GRPO_ROWS_FWD_LAUNCH (forward-type kernels), GRPO_ROWS_BWD_LAUNCH
 // (backward-type kernels), GRPO_ROWS_LAUNCH (both).  Unset: built-in policy.
