@@ -620,7 +620,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
       if (m >= g.M) continue;
       float* p = Cp + int64_t(m) * g.ldc + n;
       if (full_n) {
-        *reinterpret_cast<f32x4*>(p) = cur[u];
+        // store mode streams C past the caches (the logits of a chunk, 1.8 GB,
+        // would otherwise evict the operand panels the product re-reads;
+        // measured 3% off a fused batch); accumulate keeps the C it just read
+        if constexpr (MODE == GEMM_STORE)
+          __builtin_nontemporal_store(cur[u], reinterpret_cast<f32x4*>(p));
+        else
+          *reinterpret_cast<f32x4*>(p) = cur[u];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
