@@ -71,69 +71,6 @@ struct Stage {
     }
   }
 
-  // Interior tiles (every chunk inside the operand): plain loads.
-  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
-                                                       int r0, int k0, v4u (&v)[NREG]) {
-    const int t = threadIdx.x;
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int c = t + NTHREADS * i;
-        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(r0 + c / (BK / 8)) * ld + k0 +
-                                             (c % (BK / 8)) * 8);
-      }
-    } else {
-      const int b = t / TPB, q = t % TPB;
-      const int kb = b % (BK / 8), rb = b / (BK / 8);
-      const uint16_t* base = P + int64_t(k0 + kb * 8 + q * KPT) * ld + r0 + rb * 8;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) v[i] = *reinterpret_cast<const v4u*>(base + int64_t(i) * ld);
-    }
-  }
-
-  // Branch-free variant for the pipelined kernel: every lane loads from a
-  // clamped, always-valid address; bit i of `ok` says whether chunk i lies
-  // inside the operand (store_masked zeroes the others).  Keeping the
-  // select out of the load lets the loads stay in flight across the MFMAs.
-  // Requires extent >= 1 (>= 8 when MN-contiguous) and kend >= 8.
-  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
-                                                      int extent, int r0, int k0, int kend,
-                                                      v4u (&v)[NREG], uint32_t& ok) {
-    const int t = threadIdx.x;
-    ok = 0u;
-    if constexpr (KC) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int c = t + NTHREADS * i;
-        const int row = r0 + c / (BK / 8), k = k0 + (c % (BK / 8)) * 8;
-        ok |= uint32_t((row < extent) && (k < kend)) << i;
-        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(row, extent - 1)) * ld +
-                                             min(k, kend - 8));
-      }
-    } else {
-      const int b = t / TPB, q = t % TPB;
-      const int kb = b % (BK / 8), rb = b / (BK / 8);
-      const int col = r0 + rb * 8;
-      const bool col_ok = col < extent;
-      const int colc = min(col, extent - 8);
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int k = k0 + kb * 8 + q * KPT + i;
-        ok |= uint32_t(col_ok && (k < kend)) << i;
-        v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(k, kend - 1)) * ld + colc);
-      }
-    }
-  }
-
-  template <int LROW>
-  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
-                                                      uint32_t ok) {
-    const v4u zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) v[i] = ((ok >> i) & 1u) ? v[i] : zero;
-    store<LROW>(lds, v);
-  }
-
   // write to an LDS tile laid out [row][k] with pitch LROW
   template <int LROW>
   __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
@@ -174,7 +111,9 @@ struct Stage {
   }
 };
 
-// Operand handling of the pipelined kernel, one ROWS x BK tile per K step.
+// Operand handling of the pipelined kernel, one ROWS x BK tile per K step,
+// staged as NREG 16-byte chunks per lane (chunk i of lane t is chunk
+// t + 256 i of the tile).
 //  K-contiguous: LDS [row][k], pitch BK + 8; a fragment is one 128-bit read.
 //  MN-contiguous: LDS [k][row], pitch ROWS + 32, filled by plain 16-byte
 //    copies (no register transpose); a fragment is two ds_read_b64_tr_b16.
@@ -184,31 +123,35 @@ struct Stage {
 //    c + 4 (q % 4) .. +3, lane i receives rows kb .. kb+3 of column c + i:
 //    the K-run the MFMA fragment wants.  The 32-element pad puts the four
 //    K-rows one read touches on disjoint bank quarters.
+// load_one_clamped reads from an always-valid address and reports whether
+// the chunk lies inside the operand (the caller stores zeros otherwise).
 template <int ROWS, int BK, bool KC>
 struct PipeOp;
 
 template <int ROWS, int BK>
 struct PipeOp<ROWS, BK, true> {
-  using S = Stage<ROWS, BK, true>;
   static constexpr int PITCH = BK + 8;
   static constexpr int ELEMS = ROWS * PITCH;
-  static constexpr int NREG = S::NREG;
+  static constexpr int CPR = BK / 8;  // 16-byte chunks per row
+  static constexpr int NREG = ROWS * CPR / NTHREADS;
   static constexpr int READS = 1;  // LDS instructions per fragment
-  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
-                                                       int r0, int k0, v4u (&v)[NREG]) {
-    S::load_interior(P, ld, r0, k0, v);
+  static_assert(NREG >= 1, "bad tile");
+  __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x + NTHREADS * i) / CPR; }
+  __device__ __forceinline__ static int k_of(int i) { return ((threadIdx.x + NTHREADS * i) % CPR) * 8; }
+  __device__ __forceinline__ static v4u load_one(const uint16_t* __restrict__ P, int64_t ld,
+                                                 int r0, int k0, int i) {
+    return *reinterpret_cast<const v4u*>(P + int64_t(r0 + row_of(i)) * ld + k0 + k_of(i));
   }
-  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
-                                                      int extent, int r0, int k0, int kend,
-                                                      v4u (&v)[NREG], uint32_t& ok) {
-    S::load_clamped(P, ld, extent, r0, k0, kend, v, ok);
+  // requires extent >= 1 and kend >= 8
+  __device__ __forceinline__ static v4u load_one_clamped(const uint16_t* __restrict__ P,
+                                                         int64_t ld, int extent, int r0, int k0,
+                                                         int kend, int i, bool& in) {
+    const int row = r0 + row_of(i), k = k0 + k_of(i);
+    in = (row < extent) && (k < kend);
+    return *reinterpret_cast<const v4u*>(P + int64_t(min(row, extent - 1)) * ld + min(k, kend - 8));
   }
-  __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
-    S::template store<PITCH>(lds, v);
-  }
-  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
-                                                      uint32_t ok) {
-    S::template store_masked<PITCH>(lds, v, ok);
+  __device__ __forceinline__ static void store_one(uint16_t* __restrict__ lds, int i, v4u v) {
+    *reinterpret_cast<v4u*>(lds + row_of(i) * PITCH + k_of(i)) = v;
   }
   // lane's fragment base for the wave's half `h` of the tile's rows
   __device__ __forceinline__ static int lane_offset(int h, int lane) {
@@ -227,45 +170,23 @@ struct PipeOp<ROWS, BK, false> {
   static constexpr int RC = ROWS / 8;  // 16-byte chunks per K-row
   static constexpr int NREG = ROWS * BK / 8 / NTHREADS;
   static constexpr int READS = 2;
-  static_assert(NREG >= 1 && NREG <= 32, "bad tile");
-  __device__ __forceinline__ static void load_interior(const uint16_t* __restrict__ P, int64_t ld,
-                                                       int r0, int k0, v4u (&v)[NREG]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int c = t + NTHREADS * i;
-      v[i] = *reinterpret_cast<const v4u*>(P + int64_t(k0 + c / RC) * ld + r0 + (c % RC) * 8);
-    }
+  static_assert(NREG >= 1, "bad tile");
+  __device__ __forceinline__ static int k_of(int i) { return (threadIdx.x + NTHREADS * i) / RC; }
+  __device__ __forceinline__ static int col_of(int i) { return ((threadIdx.x + NTHREADS * i) % RC) * 8; }
+  __device__ __forceinline__ static v4u load_one(const uint16_t* __restrict__ P, int64_t ld,
+                                                 int r0, int k0, int i) {
+    return *reinterpret_cast<const v4u*>(P + int64_t(k0 + k_of(i)) * ld + r0 + col_of(i));
   }
   // requires extent % 8 == 0, extent >= 8 and kend >= 1
-  __device__ __forceinline__ static void load_clamped(const uint16_t* __restrict__ P, int64_t ld,
-                                                      int extent, int r0, int k0, int kend,
-                                                      v4u (&v)[NREG], uint32_t& ok) {
-    const int t = threadIdx.x;
-    ok = 0u;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int c = t + NTHREADS * i;
-      const int k = k0 + c / RC, row = r0 + (c % RC) * 8;
-      ok |= uint32_t((row < extent) && (k < kend)) << i;
-      v[i] = *reinterpret_cast<const v4u*>(P + int64_t(min(k, kend - 1)) * ld +
-                                           min(row, extent - 8));
-    }
+  __device__ __forceinline__ static v4u load_one_clamped(const uint16_t* __restrict__ P,
+                                                         int64_t ld, int extent, int r0, int k0,
+                                                         int kend, int i, bool& in) {
+    const int k = k0 + k_of(i), row = r0 + col_of(i);
+    in = (row < extent) && (k < kend);
+    return *reinterpret_cast<const v4u*>(P + int64_t(min(k, kend - 1)) * ld + min(row, extent - 8));
   }
-  __device__ __forceinline__ static void store(uint16_t* __restrict__ lds, const v4u (&v)[NREG]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int c = t + NTHREADS * i;
-      *reinterpret_cast<v4u*>(lds + (c / RC) * PITCH + (c % RC) * 8) = v[i];
-    }
-  }
-  __device__ __forceinline__ static void store_masked(uint16_t* __restrict__ lds, v4u (&v)[NREG],
-                                                      uint32_t ok) {
-    const v4u zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) v[i] = ((ok >> i) & 1u) ? v[i] : zero;
-    store(lds, v);
+  __device__ __forceinline__ static void store_one(uint16_t* __restrict__ lds, int i, v4u v) {
+    *reinterpret_cast<v4u*>(lds + k_of(i) * PITCH + col_of(i)) = v;
   }
   // lane l (group G = l / 16, q = l % 16) points at K-row 8 (G / 2) + q / 4,
   // column 16 (G % 2) + 4 (q % 4) of its wave's half of the rows
@@ -380,154 +301,148 @@ __global__ __launch_bounds__(NTHREADS, C::WPE) void gemm_bf16_kernel(GemmArgs g)
   }
 }
 
-// Interleave one sub-step's 16 MFMAs with NR LDS fragment reads (8, 12 or
-// 16) and, when VMEM, the 16 global loads of the next tile.
-template <int NR, bool VMEM>
-__device__ __forceinline__ void sched_reads() {
-  static_assert(NR == 8 || NR == 12 || NR == 16, "reads per sub-step");
-  if constexpr (NR == 8) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
-    }
-  } else if constexpr (NR == 12) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if constexpr (VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-    }
+// Spread U = 0 .. NU-1 MFMAs evenly over R LDS reads, W LDS writes and V
+// global loads (one MFMA, then its share of each), for sched_group_barrier.
+template <int U, int NU, int R, int W, int V>
+__device__ __forceinline__ void sched_mix() {
+  if constexpr (U < NU) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int r = (R * (U + 1)) / NU - (R * U) / NU;
+    constexpr int w = (W * (U + 1)) / NU - (W * U) / NU;
+    constexpr int v = (V * (U + 1)) / NU - (V * U) / NU;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);  // DS write
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // VMEM read
+    sched_mix<U + 1, NU, R, W, V>();
   }
 }
 
-// K loop of the pipelined kernel; EDGE selects masked loads (tiles that
-// overhang M, N or the K range) over plain ones.  Per K step (4 sub-steps of
-// 16): each sub-step reads the next sub-step's fragments from LDS into a
-// second register set while its 16 MFMAs run; the staged next step is
-// written to the other LDS buffer during sub-step 2; one barrier ends the
-// step.  The global loads for the next step are issued at sub-step 0 (half a
-// step of latency cover), or with DEEP right after the sub-step-2 store for
-// the step after next (a full step; the prologue then loads two steps).  The
-// body has no branches, and sched_group_barrier interleaves the memory
-// instructions with the MFMAs.
-template <class C, bool A_KC, bool B_KC, bool EDGE, bool DEEP>
+// K loop of the pipelined kernel; EDGE selects clamped, masked staging
+// (tiles that overhang M, N or the K range) over plain loads.  A K step on
+// LDS buffer b is four 16-deep sub-steps of 16 MFMAs, each fed by fragments
+// read during the sub-step before:
+//  sub-steps 0-2 also write a third of the next step's staged chunks into
+//    buffer b^1 and, into each register just written out, load the chunk of
+//    the step after next (a full step of latency cover), so that no
+//    sub-step carries a burst of LDS writes or global loads;
+//  a barrier then makes b^1 whole (and ends every read of b);
+//  sub-step 3 reads the next step's first fragments from b^1, so nothing
+//    waits on LDS after the barrier.
+// The body has no branches; sched_group_barrier interleaves the memory
+// instructions with the MFMAs and sched_barrier keeps the sub-steps apart.
+template <class C, bool A_KC, bool B_KC, bool EDGE>
 __device__ __forceinline__ void pipe_mainloop(
     const GemmArgs& g, int m0, int n0, int kbeg, int kend,
     uint16_t (*As)[PipeOp<C::BM, C::BK, A_KC>::ELEMS],
     uint16_t (*Bs)[PipeOp<C::BN, C::BK, B_KC>::ELEMS], f32x16 (&acc)[C::TM][C::TN]) {
   constexpr int BK = C::BK, TM = C::TM, TN = C::TN;
-  constexpr int NS = BK / 16;
+  static_assert(BK == 64, "four 16-deep sub-steps per K step");
   using OA = PipeOp<C::BM, BK, A_KC>;
   using OB = PipeOp<C::BN, BK, B_KC>;
-  constexpr int NR = TM * OA::READS + TN * OB::READS;
+  constexpr int NA = OA::NREG, NW = NA + OB::NREG;
+  static_assert(NW <= 32, "one in-bounds bit per chunk");
+  constexpr int NR = TM * OA::READS + TN * OB::READS;  // LDS reads per sub-step
+  // chunks written (and reloaded) in sub-steps 0, 1, 2: [0, W1), [W1, W2), [W2, NW)
+  constexpr int W1 = (NW + 2) / 3, W2 = W1 + (NW - W1 + 1) / 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  v4u ra[OA::NREG], rb[OB::NREG];
-  uint32_t oka = ~0u, okb = ~0u;
-  auto load = [&](int k) {
+  v4u r[NW];
+  uint32_t in_bits = ~0u;
+  auto load_chunk = [&](int c, int k) {
     if constexpr (EDGE) {
-      OA::load_clamped(g.A, g.lda, g.M, m0, k, kend, ra, oka);
-      OB::load_clamped(g.B, g.ldb, g.N, n0, k, kend, rb, okb);
+      bool in;
+      if (c < NA) r[c] = OA::load_one_clamped(g.A, g.lda, g.M, m0, k, kend, c, in);
+      else r[c] = OB::load_one_clamped(g.B, g.ldb, g.N, n0, k, kend, c - NA, in);
+      in_bits = in ? (in_bits | (1u << c)) : (in_bits & ~(1u << c));
     } else {
-      OA::load_interior(g.A, g.lda, m0, k, ra);
-      OB::load_interior(g.B, g.ldb, n0, k, rb);
+      if (c < NA) r[c] = OA::load_one(g.A, g.lda, m0, k, c);
+      else r[c] = OB::load_one(g.B, g.ldb, n0, k, c - NA);
     }
   };
-  auto store = [&](int b) {
-    if constexpr (EDGE) {
-      OA::store_masked(As[b], ra, oka);
-      OB::store_masked(Bs[b], rb, okb);
-    } else {
-      OA::store(As[b], ra);
-      OB::store(Bs[b], rb);
-    }
+  auto store_chunk = [&](int c, int b) {
+    v4u v = r[c];
+    if constexpr (EDGE) v = ((in_bits >> c) & 1u) ? v : v4u{0u, 0u, 0u, 0u};
+    if (c < NA) OA::store_one(As[b], c, v);
+    else OB::store_one(Bs[b], c - NA, v);
   };
-  const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
-  load(kbeg);
-  store(0);
-  if constexpr (DEEP) load(min(kbeg + BK, last));
-  __syncthreads();
-
   const int a_off = OA::lane_offset(wm, lane);
   const int b_off = OB::lane_offset(wn, lane);
   bf16x8 fa[2][TM], fb[2][TN];
+  auto frags = [&](int set, int b, int s) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(As[0], a_off, i, 0);
+    for (int i = 0; i < TM; ++i) fa[set][i] = OA::frag(As[b], a_off, i, s);
 #pragma unroll
-  for (int jj = 0; jj < TN; ++jj) fb[0][jj] = OB::frag(Bs[0], b_off, jj, 0);
+    for (int jj = 0; jj < TN; ++jj) fb[set][jj] = OB::frag(Bs[b], b_off, jj, s);
+  };
+  // operands swapped (B fragment as the row operand): see the epilogue
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][jj], fa[set][i],
+                                                            acc[i][jj], 0, 0, 0);
+  };
 
-  int buf = 0;
+  // the last steps reload the final step's tile (in bounds, never used)
+  const int last = ((kend - 1 - kbeg) / BK) * BK + kbeg;
+#pragma unroll
+  for (int c = 0; c < NW; ++c) load_chunk(c, kbeg);
+#pragma unroll
+  for (int c = 0; c < NW; ++c) store_chunk(c, 0);
+  const int k1 = min(kbeg + BK, last);
+#pragma unroll
+  for (int c = 0; c < NW; ++c) load_chunk(c, k1);
+  __syncthreads();
+  frags(0, 0, 0);
+
+  int b = 0;
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    // next tile (the last step reloads its own tile; that copy is never read)
-    if constexpr (!DEEP) load(min(k0 + BK, last));
+    const int k2 = min(k0 + 2 * BK, last);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(1, b, 1);
+    mfmas(0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s + 1 < NS) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = OA::frag(As[buf], a_off, i, s + 1);
-#pragma unroll
-        for (int jj = 0; jj < TN; ++jj) fb[nxt][jj] = OB::frag(Bs[buf], b_off, jj, s + 1);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < TN; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jj], fa[cur][i],
-                                                              acc[i][jj], 0, 0, 0);
-      if (s == 2) {
-        store(buf ^ 1);
-        // DEEP: the loads for two steps ahead follow the store, a full step
-        // of latency cover (the tail reloads the last step, never read)
-        if constexpr (DEEP) load(min(k0 + 2 * BK, last));
-      }
-      // interleave the memory instructions with the MFMAs
-      if (s == 0) {
-        sched_reads<NR, !DEEP>();
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      } else if (s == 1) {
-        sched_reads<NR, false>();
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      } else if (s == 2) {
-        sched_reads<NR, false>();
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
-          if constexpr (DEEP) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      }
+    for (int c = 0; c < W1; ++c) {
+      store_chunk(c, b ^ 1);
+      load_chunk(c, k2);
     }
+    sched_mix<0, 8, NR, 0, 0>();
+    sched_mix<0, 8, 0, W1, W1>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, b, 2);
+    mfmas(1);
+#pragma unroll
+    for (int c = W1; c < W2; ++c) {
+      store_chunk(c, b ^ 1);
+      load_chunk(c, k2);
+    }
+    sched_mix<0, 8, NR, 0, 0>();
+    sched_mix<0, 8, 0, W2 - W1, W2 - W1>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(1, b, 3);
+    mfmas(0);
+#pragma unroll
+    for (int c = W2; c < NW; ++c) {
+      store_chunk(c, b ^ 1);
+      load_chunk(c, k2);
+    }
+    sched_mix<0, 8, NR, 0, 0>();
+    sched_mix<0, 8, 0, NW - W2, NW - W2>();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    buf ^= 1;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(As[buf], a_off, i, 0);
-#pragma unroll
-    for (int jj = 0; jj < TN; ++jj) fb[0][jj] = OB::frag(Bs[buf], b_off, jj, 0);
+    frags(0, b ^ 1, 0);
+    mfmas(1);
+    sched_mix<0, 8, NR, 0, 0>();
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    b ^= 1;
   }
 }
 
 // Software-pipelined kernel for the 256 x 256 x 64 tile (one wave per SIMD,
 // so the wave itself must hide every latency; see pipe_mainloop).
-template <class C, bool A_KC, bool B_KC, int MODE, bool DEEP>
+template <class C, bool A_KC, bool B_KC, int MODE>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, TM = C::TM, TN = C::TN;
   static_assert(BK == 64 && TM == 4 && TN == 4, "pipelined kernel expects 256 x 256 x 64");
@@ -560,8 +475,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
 
   if (kend > kbeg) {
     const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && ((kend - kbeg) % BK == 0);
-    if (interior) pipe_mainloop<C, A_KC, B_KC, false, DEEP>(g, m0, n0, kbeg, kend, As, Bs, acc);
-    else pipe_mainloop<C, A_KC, B_KC, true, DEEP>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    if (interior) pipe_mainloop<C, A_KC, B_KC, false>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    else pipe_mainloop<C, A_KC, B_KC, true>(g, m0, n0, kbeg, kend, As, Bs, acc);
   }
 
   // Epilogue.  The MFMAs ran with the operands swapped (B fragment as the
@@ -644,14 +559,10 @@ hipError_t launch_pipe(int mode, GemmArgs g, int splits, hipStream_t s) {
   g.tiles_m = (g.M + C::BM - 1) / C::BM;
   g.tiles_n = (g.N + C::BN - 1) / C::BN;
   const dim3 grid(unsigned(g.tiles_m * g.tiles_n), unsigned(splits));
-  // loads two steps ahead where it measured faster: products with an
-  // MN-contiguous operand (dz W and dz^T h, 64 and ~300 K steps per tile);
-  // the logits product (16 steps per tile) keeps the one-step form
-  constexpr bool DEEP = !(A_KC && B_KC);
   if (mode == GEMM_ACCUM)
-    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_ACCUM, DEEP>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_ACCUM>), grid, dim3(NTHREADS), 0, s, g);
   else
-    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_STORE, DEEP>), grid, dim3(NTHREADS), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<C, A_KC, B_KC, GEMM_STORE>), grid, dim3(NTHREADS), 0, s, g);
   return hipGetLastError();
 }
 

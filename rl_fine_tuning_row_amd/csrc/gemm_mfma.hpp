@@ -17,9 +17,10 @@
 //  * 256 x 128 x 32 at two workgroups per CU for mid-size products with a
 //    transposed operand;
 //  * 128 x 128 x 32 for small problems.
-// Tiles are staged global -> registers -> LDS, double buffered:
-// the next tile's global loads are in flight while the current one feeds
-// the MFMAs.  In the pipelined tile a K-contiguous operand sits in LDS as
+// Tiles are staged global -> registers -> LDS, double buffered: the next
+// K step's global loads are in flight while the current one feeds the
+// MFMAs (in the pipelined tile the loads run two steps ahead, spread chunk
+// by chunk over the step).  In the pipelined tile a K-contiguous operand sits in LDS as
 // [row][k] (16-byte pad; a fragment is one 128-bit read) and an
 // MN-contiguous one as [k][row], copied as is and read back transposed by
 // ds_read_b64_tr_b16 (two per fragment).  The two smaller tiles keep every
