@@ -391,9 +391,14 @@ __device__ __forceinline__ void pipe_mainloop(
   for (int c = 0; c < NW; ++c) load_chunk(c, kbeg);
 #pragma unroll
   for (int c = 0; c < NW; ++c) store_chunk(c, 0);
+  // the second step's loads in chunk order, after the stores: the loop then
+  // finds them outstanding in the order its own loads leave them, and waits
+  // for each chunk only as long as needed
+  __builtin_amdgcn_sched_barrier(0);
   const int k1 = min(kbeg + BK, last);
 #pragma unroll
   for (int c = 0; c < NW; ++c) load_chunk(c, k1);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   frags(0, 0, 0);
 
