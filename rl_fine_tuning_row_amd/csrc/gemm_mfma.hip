@@ -491,6 +491,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   // its 128 x 128 tile at a time in its own LDS slice (16-byte writes), reads
   // it back as whole rows and writes C with 16-byte stores, two 512-byte
   // rows per instruction (the accumulate mode loads C the same way first).
+  // Tiles inside C take a path with no per-row checks: the checked one
+  // costs several thousand scalar and branch instructions per tile.
   __syncthreads();  // every wave is done with the operand tiles
   constexpr int EP = 128 + 4;  // staging pitch in floats
   static_assert(4 * 32 * EP * 4 <= int(sizeof(As)), "staging fits the A tiles");
@@ -499,9 +501,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   const int mw = m0 + wm * (BM / 2), nw = n0 + wn * (BN / 2);
   const int col = 4 * (lane & 31);
   const int n = nw + col;
-  const bool full_n = g.vec_c && (n + 3 < g.N);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  auto stage_block = [&](int i) {
 #pragma unroll
     for (int jj = 0; jj < TN; ++jj)
 #pragma unroll
@@ -510,7 +510,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
                          acc[i][jj][4 * q + 3]};
         *reinterpret_cast<f32x4*>(stage + (lane & 31) * EP + 32 * jj + 8 * q + 4 * (lane >> 5)) = v;
       }
-    // rows 2 u + lane / 32 of the block, columns 4 (lane % 32) .. +3
+  };
+  // rows 2 u + lane / 32 of block i, columns 4 (lane % 32) .. +3
+  auto staged = [&](int u) {
+    return *reinterpret_cast<const f32x4*>(stage + (2 * u + (lane >> 5)) * EP + col);
+  };
+  // store mode streams C past the caches (the logits of a chunk, 1.8 GB,
+  // would otherwise evict the operand panels the product re-reads; measured
+  // 3% off a fused batch); accumulate keeps the C it just read
+  auto put = [&](float* p, const f32x4& v) {
+    if constexpr (MODE == GEMM_STORE) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = v;
+  };
+  if (g.vec_c && m0 + BM <= g.M && n0 + BN <= g.N) {
+    const int64_t pair = 2 * g.ldc;  // two rows per instruction
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      stage_block(i);
+      float* p0 = Cp + int64_t(mw + 32 * i + (lane >> 5)) * g.ldc + n;
+      f32x4 cur[16];
+      if constexpr (MODE == GEMM_ACCUM) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) cur[u] = *reinterpret_cast<const f32x4*>(p0 + u * pair);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if constexpr (MODE == GEMM_ACCUM) cur[u] += staged(u);
+        else cur[u] = staged(u);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) put(p0 + u * pair, cur[u]);
+    }
+    return;
+  }
+  const bool full_n = g.vec_c && (n + 3 < g.N);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    stage_block(i);
     f32x4 cur[16];
     if constexpr (MODE == GEMM_ACCUM) {
 #pragma unroll
@@ -530,9 +566,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stage + (2 * u + (lane >> 5)) * EP + col);
-      if constexpr (MODE == GEMM_ACCUM) cur[u] += v;
-      else cur[u] = v;
+      if constexpr (MODE == GEMM_ACCUM) cur[u] += staged(u);
+      else cur[u] = staged(u);
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -540,13 +575,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
       if (m >= g.M) continue;
       float* p = Cp + int64_t(m) * g.ldc + n;
       if (full_n) {
-        // store mode streams C past the caches (the logits of a chunk, 1.8 GB,
-        // would otherwise evict the operand panels the product re-reads;
-        // measured 3% off a fused batch); accumulate keeps the C it just read
-        if constexpr (MODE == GEMM_STORE)
-          __builtin_nontemporal_store(cur[u], reinterpret_cast<f32x4*>(p));
-        else
-          *reinterpret_cast<f32x4*>(p) = cur[u];
+        put(p, cur[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
