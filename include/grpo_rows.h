@@ -228,12 +228,14 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  * fused_linear_grpo_chunk -- one batch chunk of the chunked fused-linear
  * GRPO loss, gradients taken during the forward [LIGER-TRL items 3-4].
  * For the chunk's R = nseq*L rows:
- *   z = hidden * weight^T (fp32, in the workspace; never the whole batch),
- *   token-level GRPO forward + backward of sum dloss*loss on z (fp32 rows),
+ *   z = hidden * weight^T (fp32 accumulation; never the whole batch),
+ *   token-level GRPO forward + backward of sum dloss*loss on z,
  *   *loss_accum += sum_r dloss[r] * loss[r],
  *   grad_hidden = dz * weight            (overwritten, fp32 [R, H]),
- *   grad_weight += dz^T * hidden         (accumulated, fp32 [V, H]),
- * with dz rounded to bf16 before the two products.  The caller loops over
+ *   grad_weight += dz^T * hidden         (accumulated, fp32 [V, H]).
+ * The forward (softmax statistics, logp, loss) works from the fp32 values
+ * of z; the backward's softmax reads z rounded to bf16 (kept in the
+ * workspace), and dz is bf16 for the two products.  The caller loops over
  * chunks; level must be GRPO_TOKEN.  Rows whose dloss is exactly 0 (padding,
  * masked tokens) add nothing to any output and are not computed: they are
  * compacted away on the device before the first product (the zero-gradient
@@ -248,8 +250,10 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  * grad_weight fp32 [V, H] (in/out)
  * workspace: device buffer of at least
  *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned; it
- *   holds the chunk's fp32 logits and bf16 dlogits (about 6 R V bytes) and
- *   the compacted rows' hidden states and inputs (about 2 R H + 32 R).
+ *   holds the chunk's bf16 logits, overwritten by its bf16 dlogits (2 R V
+ *   bytes), the per-row softmax statistics (12 R bytes per 128 columns of
+ *   V, later reused for grad_hidden's split-K partial sums) and the
+ *   compacted rows' hidden states and inputs (about 2 R H + 36 R).
  * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,
  * weight and grad_hidden 16-byte aligned.  The result is deterministic.
  * ------------------------------------------------------------------------ */

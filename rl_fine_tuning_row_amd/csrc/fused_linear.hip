@@ -8,9 +8,14 @@
 //   0. compaction                 the rows whose weight dloss is nonzero, in
 //                                 order (one workgroup), their h rows and
 //                                 per-row inputs gathered; Rc of them
-//   1. z  = h_c W^T               MFMA GEMM, fp32 [Rc, V] in the workspace
-//   2. row forward on z           lse, logp, per-token loss (fp32 rows)
-//   3. row backward on z          dz = g/T (onehot - p) as bf16 [Rc, V]
+//   1. z  = h_c W^T               MFMA GEMM; its epilogue keeps the fp32
+//                                 accumulators for each row's softmax
+//                                 statistics over every 128-column half-tile
+//                                 and the target logit, and writes z as
+//                                 bf16 [Rc, V] to the workspace
+//   2. row forward                the partial statistics merged in a fixed
+//                                 order: lse, logp, per-token loss (fp32)
+//   3. row backward on bf16 z     dz = g/T (onehot - p) as bf16, in place
 //   4. loss_accum += sum dloss * loss     (one workgroup, fixed order)
 //   5. grad_hidden = dz W         MFMA GEMM split over V, partial sums reduced
 //                                 in a fixed order (deterministic) and
@@ -23,8 +28,10 @@
 // into the chunked products.  (Non-finite inputs on such a row are dropped
 // with it instead of propagating through 0 * inf.)  Rc is only known on the
 // device: every later launch is sized for R and reads Rc there.
-// z stays fp32 so the per-token loss meets a 1e-5 relative bar; dz is
-// rounded to bf16 before the two products (the matrix cores' input type).
+// The statistics, logp and loss come from the fp32 accumulators, so the
+// per-token loss meets a 1e-5 relative bar; the backward's softmax reads the
+// bf16 copy of z (the model's logits dtype), and dz is bf16 for the two
+// products (the matrix cores' input type).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -41,7 +48,7 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t z_off, dz_off, logp_off, lse_off, loss_off;
+  size_t z_off, part_off, zy_off, logp_off, lse_off, loss_off;
   size_t map_off, pos_off, cnt_off, hc_off, ids_off, old_off, ref_off, adv_off, w_off;
   size_t total;
   int splits;
@@ -59,16 +66,17 @@ int pick_splits(int64_t R, int64_t H) {
 WsLayout ws_layout(int64_t R, int64_t V, int64_t H) {
   WsLayout w{};
   w.splits = pick_splits(R, H);
-  const size_t zb = size_t(R) * size_t(V) * 4;
-  const size_t part = size_t(w.splits) * size_t(R) * size_t(H) * 4;
+  const size_t stats = size_t(3) * size_t(logits_halves(V)) * size_t(R) * 4;
+  const size_t splitk = size_t(w.splits) * size_t(R) * size_t(H) * 4;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += align256(bytes);
     return at;
   };
-  w.z_off = take(std::max(zb, part));  // z, later reused for the split-K partial sums
-  w.dz_off = take(size_t(R) * size_t(V) * 2);
+  w.z_off = take(size_t(R) * size_t(V) * 2);  // bf16 z, then dz in place
+  w.part_off = take(std::max(stats, splitk));  // row statistics, then split-K partial sums
+  w.zy_off = take(size_t(R) * 4);
   w.logp_off = take(size_t(R) * 4);
   w.lse_off = take(size_t(R) * 4);
   w.loss_off = take(size_t(R) * 4);
@@ -250,8 +258,10 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   if (workspace_bytes < w.total) return GRPO_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
-  float* z = reinterpret_cast<float*>(base + w.z_off);
-  uint16_t* dz = reinterpret_cast<uint16_t*>(base + w.dz_off);
+  uint16_t* z = reinterpret_cast<uint16_t*>(base + w.z_off);
+  uint16_t* dz = z;  // the backward overwrites z in place
+  float* part = reinterpret_cast<float*>(base + w.part_off);
+  float* zy = reinterpret_cast<float*>(base + w.zy_off);
   float* logp = reinterpret_cast<float*>(base + w.logp_off);
   float* lse = reinterpret_cast<float*>(base + w.lse_off);
   float* loss = reinterpret_cast<float*>(base + w.loss_off);
@@ -274,24 +284,30 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
                      h_c);
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
 
-  // 1. logits of the kept rows
+  // 1. logits of the kept rows: bf16 z, row statistics and target logits
+  const float cscale = kLog2e / p->temperature;
   GemmArgs g1{};
   g1.A = h_c;
   g1.lda = H;
   g1.B = W;
   g1.ldb = H;
-  g1.C = z;
   g1.ldc = V;
   g1.M = int32_t(R);
   g1.N = int32_t(V);
   g1.K = int32_t(H);
   g1.k_per_split = int32_t(H);
   g1.dev_m = cnt;
-  if (gemm_bf16(true, true, GEMM_STORE, g1, 1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
+  g1.z16 = z;
+  g1.stat = part;
+  g1.stat_ld = R;
+  g1.ids = ids_c;
+  g1.zy = zy;
+  g1.cscale = cscale;
+  if (gemm_bf16_logits(g1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
 
-  // 2. forward row pass on the fp32 logits (compact rows: one token per "sequence")
+  // 2. forward from the statistics (compact rows: one token per "sequence")
   FwdArgs fa{};
-  fa.logits = z;
+  fa.logits = nullptr;
   fa.ld = V;
   fa.V = int32_t(V);
   fa.L = 1;
@@ -300,7 +316,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   fa.ref_logp = ref_logp != nullptr ? ref_c : nullptr;
   fa.adv = adv_c;
   fa.T = p->temperature;
-  fa.c = kLog2e / p->temperature;
+  fa.c = cscale;
   fa.beta = p->beta;
   fa.lo = 1.0f - p->eps_low;
   fa.hi = 1.0f + p->eps_high;
@@ -310,10 +326,10 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   fa.logp = logp;
   fa.lse = lse;
   fa.dev_rows = cnt;
-  st = launch_fwd(fa, GRPO_F32, R, false, s);
+  st = launch_fwd_partials(fa, part, logits_halves(V), R, zy, R, s);
   if (st != GRPO_OK) return st;
 
-  // 3. backward row pass: bf16 dz
+  // 3. backward row pass: bf16 dz over bf16 z, in place
   BwdArgs ba{};
   ba.logits = z;
   ba.ld = V;
@@ -337,14 +353,14 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   ba.mode = BWD_GRPO;
   ba.level = GRPO_TOKEN;
   ba.dev_rows = cnt;
-  st = launch_bwd_f32_to_bf16(ba, R, s);
+  st = launch_bwd(ba, GRPO_BF16, R, s);
   if (st != GRPO_OK) return st;
 
   // 4. loss of the chunk
   hipLaunchKernelGGL(weighted_sum_kernel, dim3(1), dim3(1024), 0, s, loss, w_c, cnt, loss_accum);
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
 
-  // 5. grad_hidden = dz W, split over V into partial sums (the z region),
+  // 5. grad_hidden = dz W, split over V into partial sums (the statistics' region),
   //    reduced in order and scattered to the original rows
   GemmArgs g2{};
   g2.A = dz;
@@ -357,14 +373,14 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   const int64_t per = (V + w.splits - 1) / w.splits;
   g2.k_per_split = int32_t(((per + 63) / 64) * 64);
   g2.split_stride = R * H;
-  g2.C = z;
+  g2.C = part;
   g2.ldc = H;
   g2.dev_m = cnt;
   if (gemm_bf16(true, false, GEMM_STORE, g2, w.splits, s) != hipSuccess) return GRPO_ERR_LAUNCH;
   {
     const int64_t n = R * H;
     hipLaunchKernelGGL(splitk_scatter_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0,
-                       s, z, w.splits, n, pos, R, int(H), grad_hidden);
+                       s, part, w.splits, n, pos, R, int(H), grad_hidden);
     if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
   }
 

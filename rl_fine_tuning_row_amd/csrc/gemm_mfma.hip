@@ -5,6 +5,7 @@
 #include "gemm_mfma.hpp"
 #include "grpo_rows.h"
 #include "host_common.hpp"
+#include "row_core.hpp"
 
 namespace grpo {
 namespace {
@@ -497,6 +498,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   constexpr int EP = 128 + 4;  // staging pitch in floats
   static_assert(4 * 32 * EP * 4 <= int(sizeof(As)), "staging fits the A tiles");
   float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * (32 * EP);
+  float* const stage0 = stage;
   float* Cp = g.C + int64_t(z) * g.split_stride;
   const int mw = m0 + wm * (BM / 2), nw = n0 + wn * (BN / 2);
   const int col = 4 * (lane & 31);
@@ -522,6 +524,76 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
     if constexpr (MODE == GEMM_STORE) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
     else *reinterpret_cast<f32x4*>(p) = v;
   };
+  if constexpr (MODE == GEMM_LOGITS) {
+    // Per 32-row block: each row's 128 columns of this wave are split
+    // between lanes l and l^32 (64 each, in registers).  Each lane folds its
+    // 64 into an online softmax state, the pair merges, and one partial per
+    // row and half-tile is written.  The block then goes through the LDS
+    // staging for the target logit of each row (fp32) and for the bf16 copy
+    // (four 256-byte row pieces per instruction; non-temporal: the row pass
+    // reads it only after the product's other tiles).
+    const float c = g.cscale;
+    const int P = 2 * g.tiles_n, p = 2 * tn + wn;
+    const int64_t sl = g.stat_ld;
+    float* pm = g.stat + int64_t(p) * sl;
+    float* ps = pm + int64_t(P) * sl;
+    float* pt = ps + int64_t(P) * sl;
+    float* stage = stage0;
+    const int cb = 8 * (lane & 15);  // first of this lane's 8 columns in a row piece
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      stage_block(i);
+      // Columns past N leave the fold.  With N % 8 == 0 that is decided per
+      // 8-column group, the same for every lane (uniform), and a wave with
+      // no column left keeps the empty state rather than fold the fill.
+      const int nv = g.N - nw;  // columns of this wave's half inside C
+      float x[4 * 16];          // x[16 jj + r] = acc[i][jj][r]
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[16 * jj + r] = 32 * jj + 8 * (r >> 2) < nv ? acc[i][jj][r] : kNegBig;
+      Stat st;
+      stat_init(st);
+      if (nv > 0) stat_tile<64, true>(st, x, c);
+      Stat o;
+      o.m = __shfl_xor(st.m, 32, 64);
+      o.s = __shfl_xor(st.s, 32, 64);
+      o.t = __shfl_xor(st.t, 32, 64);
+      st = stat_merge<true>(st, o, c);
+      if (lane < 32) {
+        const int m = mw + 32 * i + lane;
+        if (m < g.M) {
+          pm[m] = st.m;
+          ps[m] = st.s;
+          pt[m] = st.t;
+          const int64_t y = g.ids[m];
+          if (y >= nw && y < nw + BN / 2 && y < g.N) g.zy[m] = stage[lane * EP + int(y - nw)];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = 4 * u + (lane >> 4);
+        const int m = mw + 32 * i + row;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(stage + row * EP + cb);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(stage + row * EP + cb + 4);
+        if (m >= g.M) continue;
+        uint16_t* q = g.z16 + int64_t(m) * g.ldc + nw + cb;
+        if (nw + cb + 8 <= g.N) {
+          const v4u w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                         pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+          __builtin_nontemporal_store(w, reinterpret_cast<v4u*>(q));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (nw + cb + e < g.N) q[e] = to_bf16(e < 4 ? a[e] : b[e - 4]);
+        }
+      }
+      // one row block at a time (interleaving them spills registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
   if (g.vec_c && m0 + BM <= g.M && n0 + BN <= g.N) {
     const int64_t pair = 2 * g.ldc;  // two rows per instruction
 #pragma unroll
@@ -650,6 +722,18 @@ hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g
   if (!(a_kcontig && b_kcontig) && mid_tiles >= 512)
     return launch_cfg<Mid>(a_kcontig, b_kcontig, mode, g, splits, s);
   return launch_cfg<Small>(a_kcontig, b_kcontig, mode, g, splits, s);
+}
+
+hipError_t gemm_bf16_logits(const GemmArgs& g0, hipStream_t s) {
+  if (g0.M == 0 || g0.N == 0) return hipSuccess;
+  GemmArgs g = g0;
+  g.vec_c = 0;
+  g.tiles_m = (g.M + Large::BM - 1) / Large::BM;
+  g.tiles_n = (g.N + Large::BN - 1) / Large::BN;
+  const dim3 grid(unsigned(g.tiles_m * g.tiles_n), 1u);
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<Large, true, true, GEMM_LOGITS>), grid,
+                     dim3(NTHREADS), 0, s, g);
+  return hipGetLastError();
 }
 
 }  // namespace grpo

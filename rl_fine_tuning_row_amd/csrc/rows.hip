@@ -71,24 +71,15 @@ __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, flo
   return st;
 }
 
-template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
-__global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
-  const int64_t r = blockIdx.x;
-  if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
-  const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
-  const Stat st = block_reduce_stat<WG, NEED_T>(
-      scan_row<TIn, WG, UNROLL, VEC, NEED_T, NTL>(row, a.V, a.c), a.c);
-  if (threadIdx.x != 0) return;
-
+// The per-row outputs of the forward from the merged statistics st and the
+// target logit zy (ignored when !valid: the row's logp is then NaN and the
+// error counted).
+template <bool NEED_T>
+__device__ __forceinline__ void fwd_token_epilogue(const FwdArgs& a, int64_t r, const Stat& st,
+                                                   float zy_in, bool valid) {
   const float logS = logf(st.s);
   const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
-  if (a.mode == FWD_ENTROPY) {
-    a.entropy[r] = H;
-    return;
-  }
-  const int64_t y = a.ids[r];
-  const bool valid = y >= 0 && y < a.V;
-  const float zy = valid ? load_elem(row + y) : __builtin_nanf("");
+  const float zy = valid ? zy_in : __builtin_nanf("");
   if (!valid && a.err_count != nullptr) atomicAdd(a.err_count, 1);
   const float lse = st.m / a.T + logS;
   const float logp = (zy - st.m) / a.T - logS;
@@ -116,6 +107,62 @@ __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
   } else {
     a.loss[r] = kl_term;  // the sequence epilogue adds the sequence's pg
   }
+}
+
+template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
+__global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
+  const int64_t r = blockIdx.x;
+  if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
+  const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
+  const Stat st = block_reduce_stat<WG, NEED_T>(
+      scan_row<TIn, WG, UNROLL, VEC, NEED_T, NTL>(row, a.V, a.c), a.c);
+  if (threadIdx.x != 0) return;
+
+  const float logS = logf(st.s);
+  const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
+  if (a.mode == FWD_ENTROPY) {
+    a.entropy[r] = H;
+    return;
+  }
+  const int64_t y = a.ids[r];
+  const bool valid = y >= 0 && y < a.V;
+  fwd_token_epilogue<NEED_T>(a, r, st, valid ? load_elem(row + y) : 0.0f, valid);
+}
+
+// Forward of the chunked loss's rows from the logits product's partial
+// statistics: lane = row (64 rows per workgroup), the NW waves each merge a
+// strided share of the row's P partials, the shares are merged in wave
+// order (deterministic), and the target logit comes from zy (fp32).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
+                                                                    const float* __restrict__ stat,
+                                                                    int P, int64_t sl,
+                                                                    const float* __restrict__ zy,
+                                                                    int64_t rows) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t r = int64_t(blockIdx.x) * 64 + lane;
+  const int64_t R = a.dev_rows != nullptr ? min(rows, int64_t(*a.dev_rows)) : rows;
+  Stat st;
+  stat_init(st);
+  if (r < R) {
+    const float* pm = stat + r;
+    const float* ps = pm + int64_t(P) * sl;
+    const float* pt = ps + int64_t(P) * sl;
+#pragma unroll 4
+    for (int p = w; p < P; p += NW) {
+      const Stat q = {pm[int64_t(p) * sl], ps[int64_t(p) * sl], pt[int64_t(p) * sl]};
+      st = stat_merge<true>(st, q, a.c);
+    }
+  }
+  __shared__ Stat sh[NW][64];
+  sh[w][lane] = st;
+  __syncthreads();
+  if (w != 0 || r >= R) return;
+#pragma unroll
+  for (int k = 1; k < NW; ++k) st = stat_merge<true>(st, sh[k][lane], a.c);
+  const int64_t y = a.ids[r];
+  const bool valid = y >= 0 && y < a.V;
+  fwd_token_epilogue<true>(a, r, st, valid ? zy[r] : 0.0f, valid);
 }
 
 // sequence level: one workgroup per sequence; mask-weighted mean log-ratio,
@@ -587,6 +634,15 @@ int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
+int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat_ld,
+                        const float* zy, int64_t rows, hipStream_t s) {
+  if (rows <= 0) return GRPO_OK;
+  constexpr int NW = 16;
+  hipLaunchKernelGGL((row_fwd_partials_kernel<NW>), dim3(unsigned((rows + 63) / 64)),
+                     dim3(64 * NW), 0, s, a, stat, P, stat_ld, zy, rows);
+  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
 int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
   const Shape sh = pick_bwd_shape(rows, a.V, es);
@@ -682,17 +738,6 @@ int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s)
   }
 #undef ENT_LAUNCH
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
-}
-
-int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s) {
-  const Shape sh = pick_bwd_shape(rows, a.V, 4);
-  // fp32 rows in 16-byte vectors, bf16 rows in 8-byte vectors
-  const bool vec = rows_vec_ok(a.logits, a.ld, 4) && aligned(a.dlogits, 8) &&
-                   ((a.ld_out * 2) % 8) == 0;
-  const bool ntl = rows * a.ld * 4 > kNtLoadBytes;
-  const hipError_t e = vec ? launch_bwd_t<float, uint16_t, true>(a, rows, sh, ntl, s)
-                           : launch_bwd_t<float, uint16_t, false>(a, rows, sh, ntl, s);
-  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
 }  // namespace grpo

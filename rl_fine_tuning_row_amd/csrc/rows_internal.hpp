@@ -70,10 +70,13 @@ struct SeqArgs {
 // Launch the forward-type row kernel (GRPO / entropy / selective
 // log-softmax, by a.mode) over `rows` rows of `dtype` logits.
 int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s);
+// Forward (FWD_GRPO, token level) of rows whose softmax statistics come as
+// P partials each (stat: m, s, t arrays of P * stat_ld floats, partial p of
+// row r at p * stat_ld + r) and whose target logit is zy[r] (fp32).
+int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat_ld,
+                        const float* zy, int64_t rows, hipStream_t s);
 // Launch the backward row kernel; logits and dlogits of the same dtype.
 int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s);
-// Backward row kernel over fp32 logits writing bf16 dlogits.
-int launch_bwd_f32_to_bf16(const BwdArgs& a, int64_t rows, hipStream_t s);
 // Entropy backward (BWD_ENTROPY) on logits and dlogits of the same dtype.
 int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s);
 
