@@ -454,18 +454,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   static_assert(BK == 64 && TM == 4 && TN == 4, "pipelined kernel expects 256 x 256 x 64");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][PipeOp<BM, BK, A_KC>::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PipeOp<BN, BK, B_KC>::ELEMS];
-  const int tiles = g.tiles_m * g.tiles_n;
-  const int id = blockIdx.x;
-  const int q = tiles / 8, rr = tiles % 8;
-  const int xcd = id % 8, j = id / 8;
-  const int t = xcd * q + min(xcd, rr) + j;
-  const int tm = t % g.tiles_m, tn = t / g.tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
-  // extents read on the device (compacted rows): tiles past them have no work
+  // extents read on the device (compacted rows): the grid is sized for the
+  // host's bound and only the tiles inside the device extent have work
   if (g.dev_m != nullptr) g.M = min(g.M, *g.dev_m);
   if (g.dev_k != nullptr) g.K = min(g.K, *g.dev_k);
-  if (m0 >= g.M) return;
-  const int z = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs in linear order.
+  // Number the active tiles of every K-split 0 .. total-1, give each XCD an
+  // equal contiguous run of them (successive m for one n and split: tiles
+  // that share a B panel share that XCD's L2) and let the rest return, so
+  // that inactive tiles (rows past the device extent) leave no XCD idle.
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int per_split = tiles_m * g.tiles_n;
+  const int total = per_split * int(gridDim.y);
+  const int id = int(blockIdx.x + gridDim.x * blockIdx.y);
+  if (id >= total) return;
+  const int q = total / 8, rr = total % 8;
+  const int xcd = id % 8, j = id / 8;
+  const int t = xcd * q + min(xcd, rr) + j;
+  const int z = t / per_split, tt = t % per_split;
+  const int tm = tt % tiles_m, tn = tt / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = z * g.k_per_split;
   const int kend = min(g.K, kbeg + g.k_per_split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
