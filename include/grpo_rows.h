@@ -251,7 +251,7 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  * workspace: device buffer of at least
  *   fused_linear_grpo_workspace_bytes(R, V, H) bytes, 256-byte aligned; it
  *   holds the chunk's bf16 logits, overwritten by its bf16 dlogits (2 R V
- *   bytes), the per-row softmax statistics (12 R bytes per 128 columns of
+ *   bytes), the per-row softmax statistics (8 R bytes per 128 columns of
  *   V, later reused for grad_hidden's split-K partial sums) and the
  *   compacted rows' hidden states and inputs (about 2 R H + 36 R).
  * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,

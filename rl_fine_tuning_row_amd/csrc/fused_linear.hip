@@ -66,7 +66,7 @@ int pick_splits(int64_t R, int64_t H) {
 WsLayout ws_layout(int64_t R, int64_t V, int64_t H) {
   WsLayout w{};
   w.splits = pick_splits(R, H);
-  const size_t stats = size_t(3) * size_t(logits_halves(V)) * size_t(R) * 4;
+  const size_t stats = size_t(2) * size_t(logits_halves(V)) * size_t(R) * 4;
   const size_t splitk = size_t(w.splits) * size_t(R) * size_t(H) * 4;
   size_t o = 0;
   auto take = [&](size_t bytes) {

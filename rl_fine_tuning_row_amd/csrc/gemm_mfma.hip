@@ -535,8 +535,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   if constexpr (MODE == GEMM_LOGITS) {
     // Per 32-row block: each row's 128 columns of this wave are split
     // between lanes l and l^32 (64 each, in registers).  Each lane folds its
-    // 64 into an online softmax state, the pair merges, and one partial per
-    // row and half-tile is written.  The block then goes through the LDS
+    // 64 into an online softmax state (max and sum; the chunked loss needs no
+    // entropy), the pair merges, and one partial per row and half-tile is
+    // written.  The block then goes through the LDS
     // staging for the target logit of each row (fp32) and for the bf16 copy
     // (four 256-byte row pieces per instruction; non-temporal: the row pass
     // reads it only after the product's other tiles).
@@ -545,7 +546,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
     const int64_t sl = g.stat_ld;
     float* pm = g.stat + int64_t(p) * sl;
     float* ps = pm + int64_t(P) * sl;
-    float* pt = ps + int64_t(P) * sl;
     float* stage = stage0;
     const int cb = 8 * (lane & 15);  // first of this lane's 8 columns in a row piece
 #pragma unroll
@@ -563,18 +563,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
           x[16 * jj + r] = 32 * jj + 8 * (r >> 2) < nv ? acc[i][jj][r] : kNegBig;
       Stat st;
       stat_init(st);
-      if (nv > 0) stat_tile<64, true>(st, x, c);
+      if (nv > 0) stat_tile<64, false>(st, x, c);
       Stat o;
       o.m = __shfl_xor(st.m, 32, 64);
       o.s = __shfl_xor(st.s, 32, 64);
-      o.t = __shfl_xor(st.t, 32, 64);
-      st = stat_merge<true>(st, o, c);
+      o.t = 0.0f;
+      st = stat_merge<false>(st, o, c);
       if (lane < 32) {
         const int m = mw + 32 * i + lane;
         if (m < g.M) {
           pm[m] = st.m;
           ps[m] = st.s;
-          pt[m] = st.t;
           const int64_t y = g.ids[m];
           if (y >= nw && y < nw + BN / 2 && y < g.N) g.zy[m] = stage[lane * EP + int(y - nw)];
         }

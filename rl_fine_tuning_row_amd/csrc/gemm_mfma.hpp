@@ -57,12 +57,12 @@ struct GemmArgs {
   int32_t vec_c;           // C rows can take 16-byte accesses (set at launch)
   const int32_t* dev_m;    // nullable: M is min(M, *dev_m), read on the device
   const int32_t* dev_k;    // nullable: K is min(K, *dev_k), read on the device
-  // GEMM_LOGITS only.  Row r's statistics over the 128-column half p of
-  // block column tn (p = 2 tn + h, P = 2 tiles_n halves) are written as
-  // m = stat[p*stat_ld + r], s = stat[(P + p)*stat_ld + r],
-  // t = stat[(2P + p)*stat_ld + r] (the Stat fields of the row kernels, in
-  // units scaled by cscale = log2(e)/T); zy[r] = C[r][ids[r]] in fp32 when
-  // ids[r] is a column of C; z16 = C as bf16 with leading dimension ldc.
+  // GEMM_LOGITS only.  Row r's softmax statistics over the 128-column half
+  // p of block column tn (p = 2 tn + h, P = 2 tiles_n halves) are written as
+  // m = stat[p*stat_ld + r] and s = stat[(P + p)*stat_ld + r] (the Stat
+  // fields of the row kernels with cscale = log2(e)/T; no entropy sum);
+  // zy[r] = C[r][ids[r]] in fp32 when ids[r] is a column of C; z16 = C as
+  // bf16 with leading dimension ldc.
   uint16_t* z16;
   float* stat;
   int64_t stat_ld;
@@ -84,7 +84,8 @@ hipError_t gemm_bf16(bool a_kcontig, bool b_kcontig, int mode, const GemmArgs& g
 
 // The logits product of the chunked loss (GEMM_LOGITS, K-contiguous A and B,
 // no split): always the pipelined 256 x 256 tile; N % 8 == 0, ldc % 8 == 0
-// and z16 16-byte aligned.  It writes logits_halves(N) partial statistics per row.
+// and z16 16-byte aligned.  It writes logits_halves(N) partial statistics
+// (two floats each) per row.
 hipError_t gemm_bf16_logits(const GemmArgs& g, hipStream_t s);
 inline int logits_halves(int64_t N) { return 2 * int((N + 255) / 256); }
 

@@ -130,9 +130,10 @@ __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
 }
 
 // Forward of the chunked loss's rows from the logits product's partial
-// statistics: lane = row (64 rows per workgroup), the NW waves each merge a
-// strided share of the row's P partials, the shares are merged in wave
-// order (deterministic), and the target logit comes from zy (fp32).
+// statistics (max and sum; no entropy): lane = row (64 rows per
+// workgroup), the NW waves each merge a strided share of the row's P
+// partials, the shares are merged in wave order (deterministic), and the
+// target logit comes from zy (fp32).
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
                                                                     const float* __restrict__ stat,
@@ -147,11 +148,10 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
   if (r < R) {
     const float* pm = stat + r;
     const float* ps = pm + int64_t(P) * sl;
-    const float* pt = ps + int64_t(P) * sl;
 #pragma unroll 4
     for (int p = w; p < P; p += NW) {
-      const Stat q = {pm[int64_t(p) * sl], ps[int64_t(p) * sl], pt[int64_t(p) * sl]};
-      st = stat_merge<true>(st, q, a.c);
+      const Stat q = {pm[int64_t(p) * sl], ps[int64_t(p) * sl], 0.0f};
+      st = stat_merge<false>(st, q, a.c);
     }
   }
   __shared__ Stat sh[NW][64];
@@ -159,10 +159,10 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
   __syncthreads();
   if (w != 0 || r >= R) return;
 #pragma unroll
-  for (int k = 1; k < NW; ++k) st = stat_merge<true>(st, sh[k][lane], a.c);
+  for (int k = 1; k < NW; ++k) st = stat_merge<false>(st, sh[k][lane], a.c);
   const int64_t y = a.ids[r];
   const bool valid = y >= 0 && y < a.V;
-  fwd_token_epilogue<true>(a, r, st, valid ? zy[r] : 0.0f, valid);
+  fwd_token_epilogue<false>(a, r, st, valid ? zy[r] : 0.0f, valid);
 }
 
 // sequence level: one workgroup per sequence; mask-weighted mean log-ratio,

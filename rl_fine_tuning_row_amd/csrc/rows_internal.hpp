@@ -70,9 +70,10 @@ struct SeqArgs {
 // Launch the forward-type row kernel (GRPO / entropy / selective
 // log-softmax, by a.mode) over `rows` rows of `dtype` logits.
 int launch_fwd(const FwdArgs& a, int dtype, int64_t rows, bool need_t, hipStream_t s);
-// Forward (FWD_GRPO, token level) of rows whose softmax statistics come as
-// P partials each (stat: m, s, t arrays of P * stat_ld floats, partial p of
-// row r at p * stat_ld + r) and whose target logit is zy[r] (fp32).
+// Forward (FWD_GRPO, token level, no entropy) of rows whose softmax
+// statistics come as P partials each (stat: m and s arrays of P * stat_ld
+// floats, partial p of row r at p * stat_ld + r) and whose target logit is
+// zy[r] (fp32).
 int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat_ld,
                         const float* zy, int64_t rows, hipStream_t s);
 // Launch the backward row kernel; logits and dlogits of the same dtype.
