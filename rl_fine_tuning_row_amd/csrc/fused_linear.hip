@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gemm_mfma.hpp"
 #include "grpo_rows.h"
@@ -46,6 +47,30 @@ namespace grpo {
 namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// A second stream per device (default priority, created on first use, kept
+// for the process) for grad_weight's product, which runs beside
+// grad_hidden's: both only read dz, and the split-K product leaves CUs idle
+// in its last round that the other product's tiles then fill.  Each call
+// forks and joins through events of its own, so concurrent callers stay
+// ordered; their side work just shares the stream.  nullptr when it cannot be
+// made (the products then run one after the other on the caller's stream).
+hipStream_t side_stream() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static hipStream_t per[kMaxDevices] = {};
+  static bool tried[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!tried[dev]) {
+    tried[dev] = true;
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess) per[dev] = st;
+    else (void)hipGetLastError();
+  }
+  return per[dev];
+}
 
 struct WsLayout {
   size_t z_off, part_off, zy_off, logp_off, lse_off, loss_off;
@@ -360,6 +385,35 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   hipLaunchKernelGGL(weighted_sum_kernel, dim3(1), dim3(1024), 0, s, loss, w_c, cnt, loss_accum);
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
 
+  // 5./6. the two gradient products, grad_weight's on the side stream
+  hipStream_t s3 = s;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (hipStream_t side = side_stream()) {
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+        hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
+        hipEventRecord(fork, s) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess) {
+      s3 = side;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  int status = GRPO_OK;
+
+  // 6. grad_weight += dz^T h_c over the kept rows
+  GemmArgs g3{};
+  g3.A = dz;
+  g3.lda = V;
+  g3.B = h_c;
+  g3.ldb = H;
+  g3.C = grad_weight;
+  g3.ldc = H;
+  g3.M = int32_t(V);
+  g3.N = int32_t(H);
+  g3.K = int32_t(R);
+  g3.k_per_split = int32_t(((R + 63) / 64) * 64);
+  g3.dev_k = cnt;
+  if (gemm_bf16(false, false, GEMM_ACCUM, g3, 1, s3) != hipSuccess) status = GRPO_ERR_LAUNCH;
+
   // 5. grad_hidden = dz W, split over V into partial sums (the statistics' region),
   //    reduced in order and scattered to the original rows
   GemmArgs g2{};
@@ -376,27 +430,19 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   g2.C = part;
   g2.ldc = H;
   g2.dev_m = cnt;
-  if (gemm_bf16(true, false, GEMM_STORE, g2, w.splits, s) != hipSuccess) return GRPO_ERR_LAUNCH;
-  {
+  if (status == GRPO_OK && gemm_bf16(true, false, GEMM_STORE, g2, w.splits, s) != hipSuccess)
+    status = GRPO_ERR_LAUNCH;
+  if (status == GRPO_OK) {
     const int64_t n = R * H;
     hipLaunchKernelGGL(splitk_scatter_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0,
                        s, part, w.splits, n, pos, R, int(H), grad_hidden);
-    if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) status = GRPO_ERR_LAUNCH;
   }
-
-  // 6. grad_weight += dz^T h_c over the kept rows
-  GemmArgs g3{};
-  g3.A = dz;
-  g3.lda = V;
-  g3.B = h_c;
-  g3.ldb = H;
-  g3.C = grad_weight;
-  g3.ldc = H;
-  g3.M = int32_t(V);
-  g3.N = int32_t(H);
-  g3.K = int32_t(R);
-  g3.k_per_split = int32_t(((R + 63) / 64) * 64);
-  g3.dev_k = cnt;
-  if (gemm_bf16(false, false, GEMM_ACCUM, g3, 1, s) != hipSuccess) return GRPO_ERR_LAUNCH;
-  return GRPO_OK;
+  // the caller's stream waits for the side stream before anything after this
+  // call (also after a failed launch: nothing may stay behind unordered)
+  if (s3 != s && (hipEventRecord(join, s3) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess))
+    status = GRPO_ERR_LAUNCH;
+  if (fork != nullptr) (void)hipEventDestroy(fork);
+  if (join != nullptr) (void)hipEventDestroy(join);
+  return status;
 }
