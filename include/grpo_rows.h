@@ -256,6 +256,10 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  *   compacted rows' hidden states and inputs (about 2 R H + 36 R).
  * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,
  * weight and grad_hidden 16-byte aligned.  The result is deterministic.
+ * grad_weight's product runs on a stream the library keeps per device
+ * (default priority, made on the first call), forked from and joined back
+ * into `stream` within the call, so work enqueued on `stream` afterwards
+ * sees every output complete.
  * ------------------------------------------------------------------------ */
 int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t H,
                             const void* weight, int64_t V, const int64_t* ids,

@@ -20,7 +20,8 @@
 //   5. grad_hidden = dz W         MFMA GEMM split over V, partial sums reduced
 //                                 in a fixed order (deterministic) and
 //                                 scattered back; dropped rows get 0
-//   6. grad_weight += dz^T h_c    MFMA GEMM accumulating into fp32
+//   6. grad_weight += dz^T h_c    MFMA GEMM accumulating into fp32, on a
+//                                 side stream beside 5, joined before return
 // A row with dloss = 0 (padding, a masked token) adds 0 to the loss and its
 // dlogp, hence its dz row and its grad_hidden row, is 0: skipping it is the
 // zero-gradient skip of the logits backward ["[Liger-Kernel] LinkedIn

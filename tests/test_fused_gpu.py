@@ -67,7 +67,7 @@ def _fused_inputs(case, logp_true):
     return old, ref
 
 
-def _run_fused(lib, case, old, ref, chunk):
+def _run_fused(lib, case, old, ref, chunk, stream=None):
     T = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
              eps_high=case.eps_high)
     h = _t(case.hidden)
@@ -84,7 +84,8 @@ def _run_fused(lib, case, old, ref, chunk):
         rs = slice(b0 * case.L, (b0 + nb) * case.L)
         lib.fused_linear_grpo_chunk(h[rs], W, ids[rs], old_t[rs], adv[b0:b0 + nb], mask[rs],
                                     dl[rs], nb, case.L, ref_logp=ref_t[rs], loss_accum=loss,
-                                    grad_hidden=gh[rs], grad_weight=gW, workspace=ws, **T)
+                                    grad_hidden=gh[rs], grad_weight=gW, workspace=ws,
+                                    stream=stream, **T)
     torch.cuda.synchronize()
     return float(loss.item()), gh.cpu().numpy(), gW
 
@@ -134,6 +135,25 @@ def test_fused_deterministic():
     old, ref = _fused_inputs(case, logp_true)
     a = _run_fused(lib, case, old, ref, 2)
     b = _run_fused(lib, case, old, ref, 2)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_fused_on_a_side_stream_of_the_caller():
+    """The chunk runs grad_weight's product on a stream of the library's own
+    and joins it back: on a caller stream other than the default one, chunk
+    after chunk with no host synchronisation between them, every output is
+    bit-identical to the default-stream run."""
+    lib = require_gpu()
+    case = synth.fused_case(B=6, L=40, H=128, V=1032, dloss="mean")
+    say("fused-linear on a non-default caller stream")
+    h = oracle.decode_bf16(case.hidden)
+    W = oracle.decode_bf16(case.weight)
+    logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
+    old, ref = _fused_inputs(case, logp_true)
+    a = _run_fused(lib, case, old, ref, 2)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        b = _run_fused(lib, case, old, ref, 2, stream=side)
     assert a[0] == b[0] and np.array_equal(a[1], b[1]) and torch.equal(a[2], b[2])
 
 
