@@ -253,6 +253,34 @@ def test_fused_skips_zero_weight_rows(chunk):
     assert (gh[dropped] == 0.0).all()
 
 
+@pytest.mark.parametrize("bad", [-1, "V"])
+def test_fused_invalid_id_on_a_kept_row(bad):
+    """An id outside [0, V) on a row that carries weight has no logit to
+    gather: like the row forward, its logp is NaN, so the loss is NaN, that
+    row's grad_hidden is NaN and (as a sum over rows) every entry of
+    grad_weight is NaN; every other row of grad_hidden is unaffected."""
+    lib = require_gpu()
+    case = synth.fused_case(B=3, L=24, H=128, V=264, dloss="sum")
+    h = oracle.decode_bf16(case.hidden)
+    W = oracle.decode_bf16(case.weight)
+    logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
+    old, ref = _fused_inputs(case, logp_true)
+    kept = np.flatnonzero(case.dloss != 0.0)
+    r = int(kept[len(kept) // 2])
+    say(f"fused-linear invalid id {bad} on kept row {r}")
+    _, gh_ok, _ = _run_fused(lib, case, old, ref, 2)
+    ids_bad = case.ids.copy()
+    ids_bad[r] = -1 if bad == -1 else case.V
+    case.ids = ids_bad
+    loss, gh, gW = _run_fused(lib, case, old, ref, 2)
+    assert np.isnan(loss)
+    assert np.isnan(gh[r]).all()
+    others = np.ones(case.N, dtype=bool)
+    others[r] = False
+    assert np.array_equal(gh[others], gh_ok[others])
+    assert torch.isnan(gW).all()
+
+
 def test_fused_all_rows_zero_weight():
     """A chunk whose weights are all 0 leaves loss_accum and grad_weight as they
     were (bit for bit) and writes grad_hidden = 0."""
