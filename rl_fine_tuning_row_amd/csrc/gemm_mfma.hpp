@@ -8,6 +8,9 @@
 //   logits       = h  W^T : A = h  [R, H]  K-contig, B = W [V, H] K-contig
 //   grad_hidden  = dz W   : A = dz [R, V]  K-contig, B = W [V, H] N-contig
 //   grad_weight += dz^T h : A = dz [R, V]  M-contig, B = h [R, H] N-contig
+// (the logits product runs in GEMM_LOGITS mode: no fp32 C; the epilogue
+// turns the fp32 accumulators into per-row softmax partials, the target
+// logit and a bf16 copy of the logits).
 //
 // Three block tiles, all 256 lanes = 4 waves in a 2 x 2 grid:
 //  * 256 x 256 x 64, software-pipelined (each wave 128 x 128 = 4 x 4
@@ -20,10 +23,10 @@
 // Tiles are staged global -> registers -> LDS, double buffered: the next
 // K step's global loads are in flight while the current one feeds the
 // MFMAs (in the pipelined tile the loads run two steps ahead, spread chunk
-// by chunk over the step).  In the pipelined tile a K-contiguous operand sits in LDS as
-// [row][k] (16-byte pad; a fragment is one 128-bit read) and an
-// MN-contiguous one as [k][row], copied as is and read back transposed by
-// ds_read_b64_tr_b16 (two per fragment).  The two smaller tiles keep every
+// by chunk over the step).  In the pipelined tile a K-contiguous operand
+// sits in LDS as [row][k] (16-byte pad; a fragment is one 128-bit read) and
+// an MN-contiguous one as [k][row], copied as is and read back transposed
+// by ds_read_b64_tr_b16 (two per fragment).  The two smaller tiles keep every
 // operand K-contiguous in LDS and transpose an MN-contiguous one while
 // staging it: each lane loads two K-rows of an 8 x 8 block and writes 8
 // (k, k+1) pairs (one v_perm_b32 each).
