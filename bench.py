@@ -21,8 +21,9 @@ Other workloads (each prints its own line; not the headline):
                 65536 x 32000 bf16 (contiguous; --strided: rows of a 2V buffer)
   fused-linear  chunked fused-linear loss over h [32768, 1024] and
                 W [151936, 1024] bf16, --chunk sequences per call (value:
-                rows/s; roofline on the GEMM flops executed, zero-weight
-                rows being skipped)
+                rows/s; roofline on the dominant kernel, the logits product
+                with its row statistics, timed alone on the first chunk's
+                kept rows; zero-weight rows are skipped)
   entropy-bwd   entropy_from_logits_bwd over the rows workload's logits,
                 plus the latency of grpo_group_advantages / grpo_loss_weights
 
@@ -497,7 +498,7 @@ def run_fused(args, torch, grl, synth):
     args.steps = steps
     ms = timed([step], steps, torch)
     # rows with dloss == 0 (padding) are compacted away before the products:
-    # the roofline prices the flops actually executed, on the kept rows
+    # GEMM rates price the flops actually executed, on the kept rows
     kept = int((case.dloss != 0.0).sum())
     flops = 3 * 2.0 * kept * case.V * case.H
     tfs = flops / (ms * 1e-3) / 1e12
@@ -510,14 +511,34 @@ def run_fused(args, torch, grl, synth):
                                  f"U{{512..1024}}",
                      "chunk_sequences": c, "workspace_bytes": ws.numel(),
                      "full_logits_fp32_bytes": case.N * case.V * 4})
+    # the dominant kernel, the logits product with its statistics epilogue,
+    # timed alone on the first chunk's kept rows: back-to-back launches
+    # between two events on the launch stream
+    rows0 = torch.nonzero(dl[:c * case.L] != 0).flatten()
+    h0 = h.index_select(0, rows0).contiguous()
+    ids0 = ids.index_select(0, rows0).contiguous()
+    rc0 = int(rows0.numel())
+    z16 = torch.empty((rc0, case.V), dtype=torch.bfloat16, device="cuda")
+    st0 = torch.empty((2, grl.logits_partials(case.V), rc0), dtype=torch.float32, device="cuda")
+    zy0 = torch.empty(rc0, dtype=torch.float32, device="cuda")
+    logits = lambda: grl.grpo_gemm_bf16_logits(h0, W, ids0, temperature=case.temperature,
+                                               z16=z16, stat=st0, zy=zy0)
+    for _ in range(3):
+        logits()
+    kms = kernel_times([[logits]], 20, torch)[0]
+    ktf = 2.0 * rc0 * case.V * case.H / (kms * 1e-3) / 1e12
+    del z16, st0, zy0
     res.update({
         "rows_kept": kept, "rows_total": case.N,
         "gemm_tflops_executed": round(tfs, 1),
         "gemm_tflops_dense_equivalent": round(dense_tfs, 1),
         "pct_mfma_peak": round(100.0 * tfs / MFMA_BF16_PEAK_TFS, 2),
-        "roofline": {"kernel": "whole chunk loop (executed GEMM flops over all time)",
-                     "bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+        "kernels": {"logits_product": {"ms": round(kms, 4), "rows": rc0,
+                                       "TFLOP/s": round(ktf, 1)}},
+        "roofline": {"kernel": f"logits product with row statistics (grpo_gemm_bf16_logits, "
+                               f"the first chunk's {rc0} kept rows x V x H)",
+                     "bound": "mfma", "achieved": round(ktf, 1), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(ktf / MFMA_BF16_PEAK_TFS, 4),
                      "traffic": None},
     })
     # per-product MFMA utilisation and rate from the stored rocprofv3 runs (4-sequence chunks)

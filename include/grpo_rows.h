@@ -287,6 +287,27 @@ int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const void* B, int 
                    int accumulate, void* stream);
 
 /* ------------------------------------------------------------------------
+ * grpo_gemm_bf16_logits -- the fused-linear chunk's logits product in the
+ * form the chunk runs it, exported so it can be tested and timed alone
+ * [LIGER-TRL items 3-4: the chunk's logits h W^T; the forward's row
+ * statistics taken from them]:  z = A B^T with K-contiguous A [M, K] (lda)
+ * and B [N, K] (ldb), fp32 accumulation, then from the fp32 values
+ *   z16[r, n]   = bf16(z[r, n])  (round to nearest even; leading dim ldz),
+ *   for each row r and 128-column half p = 0 .. P-1, P = 2 ceil(N / 256):
+ *     stat[p*M + r]       = m = max of z[r, n] over n in [128p, 128p+128) and < N,
+ *     stat[(P + p)*M + r] = sum of exp((z[r, n] - m) / T) over those n
+ *     (m = -1e30 and the sum 0 when the half holds no column),
+ *   zy[r] = z[r, ids[r]] when 0 <= ids[r] < N (else zy[r] is not written).
+ * Merging a row's P partials gives its log-sum-exp of z / T.
+ * A, B, z16 bf16 and 16-byte aligned; lda, ldb, ldz multiples of 8 with
+ * lda, ldb >= K and ldz >= N; K and N multiples of 8; ids int64 [M]; stat
+ * fp32 [2 P M]; zy fp32 [M]; temperature > 0 and finite.
+ * ------------------------------------------------------------------------ */
+int grpo_gemm_bf16_logits(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                          int64_t N, int64_t K, float temperature, const int64_t* ids,
+                          void* z16, int64_t ldz, float* stat, float* zy, void* stream);
+
+/* ------------------------------------------------------------------------
  * entropy_from_logits_bwd -- backward of the per-row entropy
  * H = -sum_j p_j log p_j, p = softmax(z / T) [AXOLOTL part 1 defines H; the
  * pages give it no backward, so this is its derivative]:

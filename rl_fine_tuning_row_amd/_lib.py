@@ -60,6 +60,8 @@ _SIGS = {
                                 ctypes.POINTER(GrpoParams), _P, _P, _P, _P, ctypes.c_size_t, _P],
     "fused_linear_grpo_workspace_bytes": [_I64, _I64, _I64],
     "grpo_gemm_bf16": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I64, _I64, _I64, _I, _P],
+    "grpo_gemm_bf16_logits": [_P, _I64, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _I64, _P, _P,
+                              _P],
     "grpo_status_string": [_I],
     "entropy_from_logits_bwd": [_P, _I, _I64, _I64, _I64, _F, _P, _P, _P, _P, _I64, _P],
     "grpo_group_advantages": [_P, _I64, _I64, _F, _I, _P, _P],
@@ -457,3 +459,43 @@ def grpo_gemm_bf16(A, B, *, a_layout=0, b_layout=0, M=None, N=None, K=None, C=No
                               _stream(stream))
     _check("grpo_gemm_bf16", st)
     return C
+
+
+def logits_partials(N: int) -> int:
+    """Number of 128-column halves P whose softmax partials grpo_gemm_bf16_logits
+    writes per row."""
+    return 2 * ((N + 255) // 256)
+
+
+def grpo_gemm_bf16_logits(A, B, ids, *, temperature=1.0, z16=None, stat=None, zy=None,
+                          stream=None):
+    """The fused chunk's logits product with its statistics epilogue:
+    A bf16 [M, K], B bf16 [N, K] (both K-contiguous), ids int64 [M].
+    Returns (z16 bf16 [M, N], stat fp32 [2, P, M] (max, sum per 128-column
+    half), zy fp32 [M])."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B need unit column stride")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError(f"inner sizes differ: {K} vs {K2}")
+    _need(ids, torch.int64, M, "ids")
+    P = logits_partials(N)
+    if z16 is None:
+        z16 = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if stat is None:
+        stat = torch.empty((2, P, M), dtype=torch.float32, device=A.device)
+    if zy is None:
+        zy = torch.full((M,), float("nan"), dtype=torch.float32, device=A.device)
+    if z16.dtype != torch.bfloat16 or z16.stride(1) != 1 or tuple(z16.shape) != (M, N):
+        raise ValueError("z16 must be bf16 [M, N] with unit column stride")
+    if stat.dtype != torch.float32 or not stat.is_contiguous() or stat.numel() != 2 * P * M:
+        raise ValueError("stat must be contiguous fp32 with 2 P M elements")
+    _need(zy, torch.float32, M, "zy")
+    st = lib().grpo_gemm_bf16_logits(_ptr(A), A.stride(0), _ptr(B), B.stride(0), M, N, K,
+                                     float(temperature), _ptr(ids), _ptr(z16), z16.stride(0),
+                                     _ptr(stat), _ptr(zy), _stream(stream))
+    _check("grpo_gemm_bf16_logits", st)
+    return z16, stat, zy

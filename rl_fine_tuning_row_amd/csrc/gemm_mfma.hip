@@ -2,6 +2,8 @@
 // gemm_mfma.hpp for the layouts, tiling and fragment layout).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "gemm_mfma.hpp"
 #include "grpo_rows.h"
 #include "host_common.hpp"
@@ -783,4 +785,44 @@ extern "C" int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const vo
   const hipError_t e = gemm_bf16(akc, bkc, accumulate ? GEMM_ACCUM : GEMM_STORE, g, 1,
                                  static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+}
+
+// C ABI: the fused chunk's logits product with its statistics epilogue,
+// exported for tests and timing (see grpo_rows.h).
+extern "C" int grpo_gemm_bf16_logits(const void* A, int64_t lda, const void* B, int64_t ldb,
+                                     int64_t M, int64_t N, int64_t K, float temperature,
+                                     const int64_t* ids, void* z16, int64_t ldz, float* stat,
+                                     float* zy, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
+    return GRPO_ERR_SHAPE;
+  if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if (!(temperature > 0.0f) || !std::isfinite(temperature)) return GRPO_ERR_PARAM;
+  if (M == 0 || N == 0) return GRPO_OK;
+  if (A == nullptr || B == nullptr || ids == nullptr || z16 == nullptr || stat == nullptr ||
+      zy == nullptr)
+    return GRPO_ERR_NULL;
+  if (K % 8 != 0 || N % 8 != 0 || K == 0) return GRPO_ERR_SHAPE;
+  if (lda % 8 != 0 || ldb % 8 != 0 || ldz % 8 != 0 || lda < K || ldb < K || ldz < N)
+    return GRPO_ERR_STRIDE;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(z16, 16) || !aligned(stat, 4) ||
+      !aligned(zy, 4) || !aligned(ids, 8))
+    return GRPO_ERR_ALIGN;
+  GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.lda = lda;
+  g.B = static_cast<const uint16_t*>(B);
+  g.ldb = ldb;
+  g.ldc = ldz;
+  g.M = int32_t(M);
+  g.N = int32_t(N);
+  g.K = int32_t(K);
+  g.k_per_split = int32_t(((K + 63) / 64) * 64);
+  g.z16 = static_cast<uint16_t*>(z16);
+  g.stat = stat;
+  g.stat_ld = M;
+  g.ids = ids;
+  g.zy = zy;
+  g.cscale = kLog2e / temperature;
+  return gemm_bf16_logits(g, static_cast<hipStream_t>(stream)) == hipSuccess ? GRPO_OK
+                                                                             : GRPO_ERR_LAUNCH;
 }

@@ -158,3 +158,22 @@ def test_launch_size_limits(L):
              ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 62, None) == SHAPE
     a = L.grpo_group_advantages
     assert a(FAKE, (1 << 31) + 4, 4, 1e-4, 1, FAKE, None) == SHAPE
+
+
+def test_gemm_logits_validation(L):
+    """The exported logits product rejects bad arguments before any launch."""
+    g = L.grpo_gemm_bf16_logits
+
+    def call(A=FAKE, lda=64, B=FAKE, ldb=64, M=100, N=256, K=64, T=1.0, ids=FAKE, z=FAKE,
+             ldz=256, stat=FAKE, zy=FAKE):
+        return g(A, lda, B, ldb, M, N, K, T, ids, z, ldz, stat, zy, None)
+
+    assert call(M=0) == OK and call(N=0) == OK            # nothing to do
+    assert call(A=None) == NULL and call(ids=None) == NULL and call(zy=None) == NULL
+    assert call(K=60, lda=64, ldb=64) == SHAPE            # K not a multiple of 8
+    assert call(N=250, ldz=256) == SHAPE                   # N not a multiple of 8
+    assert call(M=-1) == SHAPE
+    assert call(lda=60) == STRIDE and call(ldz=200) == STRIDE and call(ldb=68) == STRIDE
+    assert call(T=0.0) == PARAM and call(T=float("nan")) == PARAM
+    assert call(z=FAKE_ODD) == ALIGN
+    assert call(M=1 << 30, N=1 << 30, ldz=1 << 30) == SHAPE  # grid past 31 bits

@@ -6,8 +6,8 @@ the accumulated C).
 Fused linear: loss within 1e-5 relative (row statistics and target logit
 from the logits product's fp32 accumulators); grad_hidden and grad_weight
 within 1e-2 relative Frobenius error per tensor (the backward's softmax reads
-the logits rounded to bf16, |z| 2^-9 / T in the exponent, and dz is rounded
-to bf16, 2^-9 relative, before the two products); rows of grad_hidden whose
+the logits rounded to bf16, |z| 2^-8 / T in the exponent, and dz is rounded
+to bf16, 2^-8 relative, before the two products); rows of grad_hidden whose
 dlogp is 0 are exactly 0.
 """
 import numpy as np
@@ -59,6 +59,67 @@ def test_gemm_layouts(a_layout, b_layout, M, N, K):
     torch.cuda.synchronize()
     err2 = np.abs(C2.cpu().numpy() - (C0.astype(np.float64) + ref))
     assert (err2 <= bound + 2.0 ** -23 * np.abs(C0)).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 1032, 136), (300, 264, 64), (40, 8, 8), (4096, 8200, 136)])
+def test_gemm_logits_mode(M, N, K):
+    """The fused chunk's logits product alone (grpo_gemm_bf16_logits): against
+    float64 products of the same bf16 values, z16 within the accumulation
+    bound plus bf16 rounding, every partial's max within the bound, the merged
+    log-sum-exp of z/T within 1e-5 relative plus the bound's effect, and the
+    target logit within the bound (rows with an out-of-range id untouched).
+    Where the fp32 store mode runs the same pipelined tile (>= 512 tiles:
+    the last shape) the results are exact against it: z16 is the correctly
+    rounded fp32 C, zy and each max are entries of C.  N = 1032 and 264 leave
+    8 and 0 columns in the last 128-column half-tile, (40, 8, 8) is a single
+    tile."""
+    lib = require_gpu()
+    say(f"gemm logits mode M={M} N={N} K={K}")
+    T = 0.9
+    rng = np.random.default_rng(M + N + K)
+    a_bits, a = _bf16(rng, (M, K))
+    b_bits, b = _bf16(rng, (N, K), 0.3)
+    ids = rng.integers(0, N, M).astype(np.int64)
+    ids[0] = -1
+    ids[min(3, M - 1)] = N
+    A, B = _t(a_bits), _t(b_bits)
+    z16, stat, zy = lib.grpo_gemm_bf16_logits(A, B, dev(ids), temperature=T)
+    C = lib.grpo_gemm_bf16(A, B)
+    torch.cuda.synchronize()
+    Z = a @ b.T
+    bound = 2 * K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T) + 1e-30
+    z16b = z16.view(torch.int16).cpu().numpy().view(np.uint16)
+    zg = oracle.decode_bf16(z16b)
+    assert (np.abs(zg - Z) <= bound + 2.0 ** -8 * (np.abs(Z) + bound)).all()  # bf16 unit roundoff 2^-8
+    Cn = C.cpu().numpy()
+    same_kernel = ((M + 255) // 256) * ((N + 255) // 256) >= 512
+    if same_kernel:
+        assert np.array_equal(z16b, synth.f32_to_bf16_bits(Cn))
+    st = stat.cpu().numpy().astype(np.float64)
+    P = lib.logits_partials(N)
+    assert st.shape == (2, P, M)
+    lse = np.full(M, -np.inf)
+    for p in range(P):
+        cols = np.arange(128 * p, min(128 * p + 128, N))
+        if cols.size == 0:
+            assert (st[0, p] == float(np.float32(-1e30))).all() and (st[1, p] == 0.0).all()
+            continue
+        m_ref = Z[:, cols].max(axis=1)
+        mb = bound[:, cols].max(axis=1)
+        assert (np.abs(st[0, p] - m_ref) <= mb).all()
+        if same_kernel:
+            assert np.array_equal(st[0, p].astype(np.float32), Cn[:, cols].max(axis=1))
+        lse = np.logaddexp(lse, st[0, p] / T + np.log(st[1, p]))
+    lse_ref = np.log(np.exp((Z - Z.max(axis=1, keepdims=True)) / T).sum(axis=1)) + Z.max(axis=1) / T
+    tol = 1e-5 * np.abs(lse_ref) + 1e-6 + 2 * bound.max(axis=1) / T
+    assert (np.abs(lse - lse_ref) <= tol).all()
+    zyn = zy.cpu().numpy()
+    ok = (ids >= 0) & (ids < N)
+    r = np.flatnonzero(ok)
+    assert (np.abs(zyn[r] - Z[r, ids[r]]) <= bound[r, ids[r]]).all()
+    if same_kernel:
+        assert np.array_equal(zyn[r], Cn[r, ids[r]])
+    assert np.isnan(zyn[~ok]).all()
 
 
 def _fused_inputs(case, logp_true):
