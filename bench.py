@@ -201,12 +201,17 @@ def run_grpo(args, torch, grl, synth, level):
         bwd, _, _ = grl.grpo_logits_bwd(z, ids, old_t, adv, B, L, out["logp"], out["lse"],
                                         dloss, mask=mask, seq_ratio=out.get("seq_ratio"),
                                         dlogits=dz, zero_row=zr, prepare=True, level=level, **kw)
+        # the backward with the all-zero path switched off, for the skip A/B
+        dense, _, _ = grl.grpo_logits_bwd(z, ids, old_t, adv, B, L, out["logp"], out["lse"],
+                                          dloss, mask=mask, seq_ratio=out.get("seq_ratio"),
+                                          dlogits=dz, zero_row=zr, prepare=True, level=level,
+                                          force_dense=True, **kw)
         one = None
         if level == "token":
             one, _, _, _ = grl.grpo_logits_fwd_bwd(z, ids, old_t, adv, B, L, dloss, mask=mask,
                                                    out=out, dlogits=dz, zero_row=zr,
                                                    prepare=True, **kw)
-        sets.append(dict(fwd=fwd, bwd=bwd, one=one, zr=zr))
+        sets.append(dict(fwd=fwd, bwd=bwd, dense=dense, one=one, zr=zr))
     two_steps = [(lambda s=s: (s["fwd"](), s["bwd"]())) for s in sets]
     for i in range(args.warmup):
         two_steps[i % len(two_steps)]()
@@ -268,9 +273,25 @@ def run_grpo(args, torch, grl, synth, level):
     })
     if level == "token":
         res["two_pass"] = two_pass
+    res["skip_ab"] = skip_ab(sets, args.steps, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_grpo(case, old, level)
     return res
+
+
+def skip_ab(sets, steps, torch, rounds=5):
+    """The backward alone with its all-zero path (A) and with every row forced
+    through the dense path (B), in interleaved A B B A rounds, as the Liger
+    GRPO-backward analysis measures it ("Review feedback"); median of the
+    per-round averages.  Outputs are identical either way (tested)."""
+    a_ms, b_ms = [], []
+    for _ in range(rounds):
+        for which in ("bwd", "dense", "dense", "bwd"):
+            (t,) = kernel_times([[s[which]] for s in sets], steps, torch)
+            (a_ms if which == "bwd" else b_ms).append(t)
+    a, b = float(np.median(a_ms)), float(np.median(b_ms))
+    return {"rounds": rounds, "order": "ABBA", "skip_ms": round(a, 5), "dense_ms": round(b, 5),
+            "speedup": round(b / a, 3), "time_saved_pct": round(100.0 * (1.0 - a / b), 1)}
 
 
 def cpu_grpo(case, old, level):
