@@ -174,19 +174,37 @@ __device__ __forceinline__ Stat wave_reduce_stat(Stat st, float c) {
 
 // merge the per-lane states of the workgroup; the result is valid in every
 // lane.  Fixed merge order, so the result is deterministic.
+// Across waves: lane i of every wave takes wave (i mod NW)'s state and an
+// xor butterfly merges the NW states; the merge is not bitwise symmetric in
+// its operands, so lanes may differ in the last bit and lane 0's result is
+// broadcast.  Every wave runs the same butterfly on the same data, so lane 0
+// holds the same bits in every wave.  (Merging all NW states in every lane
+// in turn keeps 3·NW floats and their temporaries live beside a
+// register-resident row.)
 template <int WG, bool NEED_T>
 __device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
   st = wave_reduce_stat<NEED_T>(st, c);
   if constexpr (WG == 64) {
     return st;
   } else {
-    __shared__ Stat sh[WG / 64];
+    constexpr int NW = WG / 64;
+    static_assert((NW & (NW - 1)) == 0, "workgroup of a power-of-two number of waves");
+    __shared__ Stat sh[NW];
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) sh[w] = st;
     __syncthreads();
-    Stat r = sh[0];
+    Stat r = sh[threadIdx.x & (NW - 1)];
 #pragma unroll
-    for (int k = 1; k < WG / 64; ++k) r = stat_merge<NEED_T>(r, sh[k], c);
+    for (int off = 1; off < NW; off <<= 1) {
+      Stat o;
+      o.m = __shfl_xor(r.m, off, 64);
+      o.s = __shfl_xor(r.s, off, 64);
+      o.t = NEED_T ? __shfl_xor(r.t, off, 64) : 0.0f;
+      r = stat_merge<NEED_T>(r, o, c);
+    }
+    r.m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.m)));
+    r.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.s)));
+    if (NEED_T) r.t = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.t)));
     return r;
   }
 }

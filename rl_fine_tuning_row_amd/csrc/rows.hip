@@ -656,9 +656,10 @@ int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
-// Single-pass launch: the row held in registers, 8 (or, past 4096 vectors,
-// 16) 16-byte vectors per lane of a 256- or 512-lane workgroup; rows longer
-// than 128 KB do not fit.
+// Single-pass launch: the row held in registers, 8 16-byte vectors per lane
+// of a 256-lane workgroup up to 2048 vectors, 4 per lane of a 1024-lane one
+// up to 4096, then 16 per lane of 512 lanes; rows longer than 128 KB do not
+// fit.
 // Returns false (nothing launched) when the row does not fit or the rows are
 // not 16-byte aligned.
 template <typename TIn, bool NEED_T>
@@ -673,6 +674,7 @@ hipError_t launch_fused_t(const FusedArgs& a, int64_t rows, int wg, int vpt, hip
   X(256, 16)
   X(512, 8)
   X(512, 16)
+  X(1024, 4)
 #undef X
   return hipErrorInvalidConfiguration;
 }
@@ -685,14 +687,15 @@ bool fused_shape(int64_t V, int es, int& wg, int& vpt) {
     vpt = o.unroll;
     return int64_t(wg) * vpt >= nvec;
   }
-  // eight vectors per lane where possible (512 x 8 measured ~1% faster than
-  // 256 x 16 on 64 KB rows), sixteen only for rows past 4096 vectors
+  // On 64 KB rows (4000 vectors, interleaved rounds on MI355X) 1024 x 4 ran
+  // 46.5 us against 47.4 for 512 x 8, 48.8 for 256 x 16 and 51.5 for
+  // 512 x 16; sixteen vectors per lane only for rows past 4096 vectors
   if (nvec <= 256 * 8) {
     wg = 256;
     vpt = 8;
-  } else if (nvec <= 512 * 8) {
-    wg = 512;
-    vpt = 8;
+  } else if (nvec <= 1024 * 4) {
+    wg = 1024;
+    vpt = 4;
   } else if (nvec <= 512 * 16) {
     wg = 512;
     vpt = 16;

@@ -76,14 +76,28 @@ def test_single_pass_token_level(with_ref, dloss):
 
 
 @pytest.mark.parametrize("dtype,V,ld_extra", [("bf16", 70008, 0), ("f32", 40000, 0),
+                                             ("bf16", 40003, 5), ("bf16", 20011, 5),
                                              ("bf16", 1003, 0), ("f32", 17, 0),
                                              ("bf16", 1003, 1)])
 def test_single_pass_shapes(dtype, V, ld_extra):
     """Rows too long for registers or not 16-byte aligned take the two-pass
-    path inside the same call; ragged tails take the single pass."""
+    path inside the same call; ragged tails on 16-byte aligned rows (input and
+    output pitch V + ld_extra) take the single pass: 5000 vectors at 512 x 16,
+    2501 at 1024 x 4."""
     lib = require_gpu()
     say(f"single-pass shapes: {dtype} V={V} ld=V+{ld_extra}")
-    _edge_case(lib, dtype, V, ld_extra, 0.9)
+    _edge_case(lib, dtype, V, ld_extra, 0.9, out_pitch=ld_extra > 0 and V > 2000)
+
+
+@pytest.mark.parametrize("shape", ["256,8", "256,16", "512,8", "512,16", "1024,4"])
+def test_single_pass_every_shape(shape, monkeypatch):
+    """Every compiled (workgroup, vectors per lane) shape of the single pass,
+    forced through the library's launch override, on a row of 2000 vectors
+    plus a 3-element tail that fits all of them."""
+    lib = require_gpu()
+    monkeypatch.setenv("GRPO_ROWS_FUSED_LAUNCH", shape)
+    say(f"single-pass shape {shape}: bf16 V=16003 ld=16008")
+    _edge_case(lib, "bf16", 16003, 5, 0.9, out_pitch=True)
 
 
 @pytest.mark.parametrize("dtype,V", [("bf16", 40), ("bf16", 1003), ("f32", 17), ("f32", 200)])
@@ -98,7 +112,7 @@ def test_single_pass_lanes_without_elements(dtype, V, T):
     _edge_case(lib, dtype, V, 0, T)
 
 
-def _edge_case(lib, dtype, V, ld_extra, T):
+def _edge_case(lib, dtype, V, ld_extra, T, out_pitch=False):
     B, L = 2, 3
     rng = np.random.default_rng(V)
     zf = (rng.standard_normal((B * L, V + ld_extra)) * 2.0).astype(np.float32)
@@ -114,7 +128,10 @@ def _edge_case(lib, dtype, V, ld_extra, T):
                           dloss=np.ones(B * L, np.float32), temperature=T, beta=0.04,
                           eps_low=0.2, eps_high=0.28, level="token")
     inp = GrpoInputs(case, lp)
-    o, dz, zr = run_single_pass(lib, t, inp)
+    dl = None
+    if out_pitch:  # dlogits with the same padded pitch as the logits
+        dl = torch.empty((B * L, V + ld_extra), dtype=t.dtype, device="cuda")[:, :V]
+    o, dz, zr = run_single_pass(lib, t, inp, dlogits=dl)
     ox, g = oracle_expectations(inp, z64, o)
     check_forward(case, ox, o)
     check_backward(case, ox, g, dz, zr, z64, inp)
