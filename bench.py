@@ -83,16 +83,24 @@ def cpu_model():
     return "unknown"
 
 
+def digest_part(workload: str) -> str:
+    """Which sources a workload's kernels come from: the fused-linear path
+    runs the GEMMs and the row kernels, every other workload the row kernels."""
+    return "all" if workload == "fused-linear" else "rows"
+
+
 def stored_counters(workload: str):
     """Per-kernel entries of the stored counter runs for a workload, if the
-    kernels have not changed since (source digest); else {}."""
+    kernels have not changed since (source digest of the workload's sources);
+    else {}."""
     from rl_fine_tuning_row_amd.build import source_digest
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return {}
     with open(path) as f:
         data = json.load(f)
-    if data.get("source_digest") != source_digest():
+    part = digest_part(workload)
+    if data.get("source_digests", {}).get(part) != source_digest(part):
         return {}
     pre = workload + ":"
     return {k[len(pre):]: v for k, v in data.get("kernels", {}).items() if k.startswith(pre)}

@@ -35,13 +35,20 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def source_digest() -> str:
+# the sources the row kernels are built from (every other file is the GEMM
+# and the fused-linear path, which also uses the row kernels)
+ROW_SOURCES = ("rows.hip", "row_core.hpp", "rows_internal.hpp", "host_common.hpp")
+
+
+def source_digest(part: str = "all") -> str:
     """sha256 over the HIP sources, their headers and the C header (identifies
-    the kernels a measurement was taken on)."""
+    the kernels a measurement was taken on).  part="rows" covers only the row
+    kernels' sources (and the C header); "all" covers every source."""
     import hashlib
     h = hashlib.sha256()
     files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                   if f.endswith((".hip", ".hpp", ".h")))
+                   if f.endswith((".hip", ".hpp", ".h"))
+                   and (part == "all" or f in ROW_SOURCES))
     files.append(os.path.join(INCLUDE, "grpo_rows.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
