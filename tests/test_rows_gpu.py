@@ -307,10 +307,12 @@ def test_entropy_and_selective_logsoftmax_full():
 # edge cases
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V,ld_extra", [(1, 0), (17, 0), (1003, 0), (4099, 0), (1003, 1), (640, 3)])
+@pytest.mark.parametrize("V,ld_extra", [(1, 0), (17, 0), (1003, 0), (4099, 0), (1003, 1), (640, 3),
+                                        (1, 7), (1003, 5), (4099, 5), (16003, 5), (40003, 5)])
 def test_ragged_and_strided_rows(dtype, V, ld_extra):
     """Tails shorter than one 128-bit vector, V = 1, and row strides that are
-    not 16-byte multiples (element-wise path)."""
+    not 16-byte multiples (element-wise path); ragged rows on 16-byte pitches
+    (ld_extra 5 and 7, fp32 1003 + 1) take the vector path with a tail."""
     lib = require_gpu()
     say(f"edge: dtype {dtype} V={V} ld=V+{ld_extra}")
     B, L = 3, 5
