@@ -26,6 +26,8 @@ Other workloads (each prints its own line; not the headline):
                 kept rows; zero-weight rows are skipped)
   entropy-bwd   entropy_from_logits_bwd over the rows workload's logits,
                 plus the latency of grpo_group_advantages / grpo_loss_weights
+  tiny          the B=2 L=16 V=1024 fp32 GRPO step (value: microseconds per
+                step, lower is better; launch-latency bound)
 
 Inputs are synthetic, generated on the host and already resident in device
 memory when the timed region starts.  ``value`` is GB/s of algorithmic HBM
@@ -59,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="grpo-token",
-                    choices=["grpo-token", "grpo-seq", "rows", "fused-linear", "entropy-bwd"])
+                    choices=["grpo-token", "grpo-seq", "rows", "fused-linear", "entropy-bwd",
+                             "tiny"])
     ap.add_argument("--sets", type=int, default=4)
     ap.add_argument("--chunk", type=int, default=4)
     ap.add_argument("--strided", action="store_true")
@@ -603,6 +606,81 @@ def run_fused(args, torch, grl, synth):
     return res
 
 
+# ---------------------------------------------------------------------------
+# tiny GRPO case (latency)
+# ---------------------------------------------------------------------------
+def run_tiny(args, torch, grl, synth):
+    """B=2 L=16 V=1024 fp32 logits, beta 0.04 with a reference, sequence 1 at
+    advantage 0: one fwd+bwd step is a few microseconds of launch latency,
+    reported as time.  The step is the single pass; the two-pass step is
+    timed beside it."""
+    case = synth.tiny_case("a")
+    logp_true = synth.load_stored_logp("tiny", case.logits[synth.stored_check_rows("tiny")])
+    old = synth.add_noise_f32(logp_true, case.old_noise)
+    ref = synth.add_noise_f32(logp_true, case.ref_noise)
+    B, L, V, N = case.B, case.L, case.V, case.N
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    z, ids, old_t, ref_t, adv, mask, dloss = (dev(case.logits), dev(case.ids), dev(old), dev(ref),
+                                              dev(case.adv), dev(case.mask), dev(case.dloss))
+    kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+              eps_high=case.eps_high)
+    dz = torch.empty((N, V), dtype=torch.float32, device="cuda")
+    zr = torch.empty(N, dtype=torch.uint8, device="cuda")
+    one, _, _, _ = grl.grpo_logits_fwd_bwd(z, ids, old_t, adv, B, L, dloss, ref_logp=ref_t,
+                                           mask=mask, dlogits=dz, zero_row=zr, prepare=True,
+                                           **kw)
+    fwd, out2 = grl.grpo_logits_fwd(z, ids, old_t, adv, B, L, ref_logp=ref_t, mask=mask,
+                                    prepare=True, **kw)
+    bwd, _, _ = grl.grpo_logits_bwd(z, ids, old_t, adv, B, L, out2["logp"], out2["lse"], dloss,
+                                    ref_logp=ref_t, mask=mask, dlogits=dz, zero_row=zr,
+                                    prepare=True, **kw)
+    for _ in range(args.warmup):
+        one()
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = timed([one], args.steps, torch)
+    (one_ms,) = kernel_times([[one]], args.steps, torch)
+    ms_two = timed([lambda: (fwd(), bwd())], args.steps, torch)
+    one()
+    torch.cuda.synchronize()
+    n_zero = int(zr.sum().item())
+    step_bytes = 2 * N * V * 4 + N * ONE_ROW_BYTES
+    gbs = step_bytes / (one_ms * 1e-3) / 1e9
+    res = base_line(args, "tiny GRPO loss fwd+bwd latency at B2 L16 V1024 fp32", ms * 1e3, "us",
+                    ms, {"workload": "token-level GRPO fwd+bwd in one pass, B=2 L=16 V=1024 fp32 "
+                                     "(T=1, beta=0.04 with a reference, eps 0.2/0.2, sequence 1 "
+                                     "at advantage 0, sum dloss)", "rows": N, "V": V,
+                         "zero_rows": n_zero, "accumulate": "fp32"}, dtype="f32")
+    res.update({
+        "higher_is_better": False,
+        "rows_per_s": round(N / (ms * 1e-3), 1),
+        "two_pass_us": round(ms_two * 1e3, 2),
+        "kernels": {"grpo_fwd_bwd": {"ms": round(one_ms, 5), "bytes": step_bytes,
+                                     "GB/s": round(gbs, 1)}},
+        "roofline": {"kernel": "grpo_fwd_bwd (launch-latency bound at 256 KiB)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    })
+    if not args.no_cpu_baseline:
+        import oracle
+        a = dict(z=case.logits.astype(np.float64), ids=case.ids, old_logp=old.astype(np.float64),
+                 ref_logp=ref.astype(np.float64), adv=case.adv, mask=case.mask, B=B, L=L,
+                 temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+                 eps_high=case.eps_high, level="token")
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and reps < 20000:
+            f = oracle.grpo_forward(**a)
+            oracle.grpo_backward(dloss=case.dloss, fwd=f, **a)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} full steps (fwd+bwd, {N} rows x {V}) in float64 "
+                                         f"NumPy, single thread; host CPU {cpu_model()}"}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -629,6 +707,8 @@ def main():
         res = run_rows(args, torch, grl, synth)
     elif args.workload == "entropy-bwd":
         res = run_entropy_bwd(args, torch, grl, synth)
+    elif args.workload == "tiny":
+        res = run_tiny(args, torch, grl, synth)
     else:
         res = run_fused(args, torch, grl, synth)
     print(json.dumps(res), flush=True)

@@ -1,6 +1,6 @@
 """Write the oracle's float64 policy log-probabilities of the seeded workloads.
 
-    python tests/golden/make_oracle_logp.py [token|sequence|fused ...]
+    python tests/golden/make_oracle_logp.py [token|sequence|tiny|fused ...]
 
 The GRPO workloads form old_logp and ref_logp as the policy's own logp plus
 noise.  That logp is the oracle's (float64, on the bf16-rounded logits; for
@@ -64,6 +64,18 @@ def make_grpo(case: synth.GrpoCase, name: str):
     return (logp, lse), meta, time.time() - t0
 
 
+def make_tiny(case: synth.GrpoCase, name: str):
+    """The tiny fp32 case (B=2 L=16 V=1024): check rows 0, 1 and the last."""
+    t0 = time.time()
+    z = case.logits
+    logp, lse = oracle.selective_log_softmax(z.astype(np.float64), case.ids, case.temperature)
+    rows = [0, 1, case.N - 1]
+    meta = {"name": name, "case": case.name, "rows": case.N, "V": case.V,
+            "check_rows": rows, "check_digest": row_digest(z[rows]),
+            "note": "oracle float64 logp and lse of the fp32 logits at the workload's temperature"}
+    return (logp, lse), meta, time.time() - t0
+
+
 def make_fused(case: synth.FusedCase, name: str):
     t0 = time.time()
     h = oracle.decode_bf16(case.hidden)
@@ -100,6 +112,10 @@ def main(which):
         logp, meta, dt = make_grpo(synth.grpo_sequence_case(), "sequence")
         save("sequence", logp, meta)
         print(f"sequence: {dt:.1f}s")
+    if "tiny" in which:
+        logp, meta, dt = make_tiny(synth.tiny_case("a"), "tiny")
+        save("tiny", logp, meta)
+        print(f"tiny: {dt:.1f}s")
     if "fused" in which:
         logp, meta, dt = make_fused(synth.fused_case(), "fused")
         save("fused", logp, meta)
@@ -107,4 +123,4 @@ def main(which):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ["token", "sequence", "fused"])
+    main(sys.argv[1:] or ["token", "sequence", "tiny", "fused"])

@@ -74,3 +74,16 @@ def test_fused_case_structure():
     assert (c.adv == 0).sum() == 2
     lens = c.mask.reshape(4, 8).sum(axis=1)
     assert (lens >= 4).all() and (lens <= 8).all()
+
+
+def test_stored_tiny_logp_is_the_oracles():
+    """The stored logp / lse of the tiny case (written by
+    tests/golden/make_oracle_logp.py from the oracle alone) equal the
+    oracle's on the generator's current inputs."""
+    import oracle
+    c = synth.tiny_case("a")
+    lp = synth.load_stored_logp("tiny", c.logits[synth.stored_check_rows("tiny")])
+    lse = synth.load_stored_lse("tiny")
+    want_lp, want_lse = oracle.selective_log_softmax(c.logits.astype(np.float64), c.ids,
+                                                     c.temperature)
+    assert np.array_equal(lp, want_lp) and np.array_equal(lse, want_lse)
