@@ -76,6 +76,8 @@ def test_single_pass_token_level(with_ref, dloss):
 
 
 @pytest.mark.parametrize("dtype,V,ld_extra", [("bf16", 70008, 0), ("f32", 40000, 0),
+                                             ("bf16", 65536, 0), ("bf16", 65544, 0),
+                                             ("f32", 32768, 0), ("f32", 32772, 0),
                                              ("bf16", 40003, 5), ("bf16", 20011, 5),
                                              ("bf16", 1003, 0), ("f32", 17, 0),
                                              ("bf16", 1003, 1)])
@@ -83,7 +85,8 @@ def test_single_pass_shapes(dtype, V, ld_extra):
     """Rows too long for registers or not 16-byte aligned take the two-pass
     path inside the same call; ragged tails on 16-byte aligned rows (input and
     output pitch V + ld_extra) take the single pass: 5000 vectors at 512 x 16,
-    2501 at 1024 x 4."""
+    2501 at 1024 x 4.  65536 bf16 / 32768 fp32 (8192 vectors) is the longest
+    row held in registers; one vector more takes the two-pass path."""
     lib = require_gpu()
     say(f"single-pass shapes: {dtype} V={V} ld=V+{ld_extra}")
     _edge_case(lib, dtype, V, ld_extra, 0.9, out_pitch=ld_extra > 0 and V > 2000)
