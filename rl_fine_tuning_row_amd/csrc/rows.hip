@@ -536,12 +536,19 @@ inline Shape pick_fwd_shape(int64_t rows, int64_t V, int es) {
   return {512, 2};
 }
 
+// Backward: 256 x 2 for short rows.  Many (more than 4096) rows of up to 4096
+// vectors (64 KB bf16) take four vectors per lane of 1024 lanes, all of a
+// lane's loads in flight at once (on 65536 x 32000: selective backward 1.31
+// ms against 1.38 at 1024 x 2, entropy backward 1.36 against 1.47); with few
+// rows (2048 x 32000) 1024 x 4 measured 3% slower.  Longer rows stream two
+// at a time (1024 x 2 was the fastest of 256 x 4/8, 512 x 2/4 and 1024 x 4
+// on 300 KB rows).
 inline Shape pick_bwd_shape(int64_t rows, int64_t V, int es) {
   const LaunchOverride o = launch_override(1);
   if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
   const int64_t nvec = V * es / 16;
   if (nvec <= 1024) return {256, 2};
-  (void)rows;
+  if (nvec <= 4096 && rows > 4096) return {1024, 4};
   return {1024, 2};
 }
 
@@ -723,24 +730,36 @@ int launch_fused(const FusedArgs& a, int dtype, int64_t rows, bool need_t, bool&
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
+template <typename T>
+hipError_t launch_bwd_entropy_t(const BwdArgs& a, int64_t rows, bool vec, Shape sh,
+                                hipStream_t s) {
+  if (!vec) {
+    hipLaunchKernelGGL((row_bwd_kernel<T, T, 256, 4, false, false, true>), dim3(unsigned(rows)),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+#define X(W, U)                                                                          \
+  if (sh.wg == W && sh.unroll == U) {                                                     \
+    hipLaunchKernelGGL((row_bwd_kernel<T, T, W, U, true, false, true>), dim3(unsigned(rows)), \
+                       dim3(W), 0, s, a);                                                 \
+    return hipGetLastError();                                                             \
+  }
+  X(256, 2)
+  X(1024, 2)
+  X(1024, 4)
+#undef X
+  return hipErrorInvalidConfiguration;
+}
+
+// the entropy backward takes the backward's shape rule (256 x 2, 1024 x 4 or
+// 1024 x 2; an override must name one of these)
 int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
   const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
-  const bool small = a.V * int64_t(es) / 16 <= 1024;  // the backward's shape rule
-#define ENT_LAUNCH(T, W, VEC_)                                                              \
-  hipLaunchKernelGGL((row_bwd_kernel<T, T, W, (VEC_ ? 2 : 4), VEC_, false, true>),         \
-                     dim3(unsigned(rows)), dim3(W), 0, s, a)
-  if (dtype == GRPO_BF16) {
-    if (!vec) ENT_LAUNCH(uint16_t, 256, false);
-    else if (small) ENT_LAUNCH(uint16_t, 256, true);
-    else ENT_LAUNCH(uint16_t, 1024, true);
-  } else {
-    if (!vec) ENT_LAUNCH(float, 256, false);
-    else if (small) ENT_LAUNCH(float, 256, true);
-    else ENT_LAUNCH(float, 1024, true);
-  }
-#undef ENT_LAUNCH
-  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+  const Shape sh = pick_bwd_shape(rows, a.V, es);
+  const hipError_t e = dtype == GRPO_BF16 ? launch_bwd_entropy_t<uint16_t>(a, rows, vec, sh, s)
+                                          : launch_bwd_entropy_t<float>(a, rows, vec, sh, s);
+  return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
 }  // namespace grpo
