@@ -17,5 +17,5 @@ def test_bench_help_lists_workloads():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0
-    for w in ("grpo-token", "grpo-seq", "rows", "fused-linear", "entropy-bwd"):
+    for w in ("grpo-token", "grpo-seq", "rows", "fused-linear", "entropy-bwd", "tiny"):
         assert w in r.stdout
