@@ -79,6 +79,7 @@ def test_single_pass_token_level(with_ref, dloss):
                                              ("bf16", 65536, 0), ("bf16", 65544, 0),
                                              ("f32", 32768, 0), ("f32", 32772, 0),
                                              ("bf16", 40003, 5), ("bf16", 20011, 5),
+                                             ("f32", 12003, 5),
                                              ("bf16", 1003, 0), ("f32", 17, 0),
                                              ("bf16", 1003, 1)])
 def test_single_pass_shapes(dtype, V, ld_extra):
@@ -92,15 +93,16 @@ def test_single_pass_shapes(dtype, V, ld_extra):
     _edge_case(lib, dtype, V, ld_extra, 0.9, out_pitch=ld_extra > 0 and V > 2000)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 16003), ("f32", 8003)])
 @pytest.mark.parametrize("shape", ["256,8", "256,16", "512,8", "512,16", "1024,4"])
-def test_single_pass_every_shape(shape, monkeypatch):
+def test_single_pass_every_shape(shape, dtype, V, monkeypatch):
     """Every compiled (workgroup, vectors per lane) shape of the single pass,
     forced through the library's launch override, on a row of 2000 vectors
-    plus a 3-element tail that fits all of them."""
+    plus a 3-element tail that fits all of them (16-byte pitch V + 5)."""
     lib = require_gpu()
     monkeypatch.setenv("GRPO_ROWS_FUSED_LAUNCH", shape)
-    say(f"single-pass shape {shape}: bf16 V=16003 ld=16008")
-    _edge_case(lib, "bf16", 16003, 5, 0.9, out_pitch=True)
+    say(f"single-pass shape {shape}: {dtype} V={V} ld={V + 5}")
+    _edge_case(lib, dtype, V, 5, 0.9, out_pitch=True)
 
 
 @pytest.mark.parametrize("dtype,V", [("bf16", 40), ("bf16", 1003), ("f32", 17), ("f32", 200)])
