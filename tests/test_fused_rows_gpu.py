@@ -106,7 +106,7 @@ def test_single_pass_every_shape(shape, dtype, V, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype,V", [("bf16", 40), ("bf16", 1003), ("f32", 17), ("f32", 200)])
-@pytest.mark.parametrize("T", [0.3, 0.5, 0.7, 1.0, 1.3, 2.0])
+@pytest.mark.parametrize("T", [0.3, 0.5, 0.7, 1.0, 1.3, 2.0, 10.0])
 def test_single_pass_lanes_without_elements(dtype, V, T):
     """Rows shorter than the workgroup leave lanes with no element.  Such a lane
     once folded its fill values into garbage sums (the rounding error of
