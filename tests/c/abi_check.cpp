@@ -4,7 +4,9 @@
 // summing to 0, all-zero rows exactly where zero_row says so (zero-advantage
 // sequence without a reference model, masked tokens), the single pass agreeing
 // with the two-pass forward + backward, the selective log-softmax and entropy
-// ops agreeing with the GRPO forward, and the small helpers' closed forms.
+// ops agreeing with the GRPO forward, the selective log-softmax backward's row
+// sums and zero rows, the fused-linear chunk's exact accumulation over two
+// calls, and the small helpers' closed forms.
 // Built by build() as tests/c/abi_check; run by tests/test_c_abi_gpu.py.
 #include <hip/hip_runtime.h>
 
@@ -200,6 +202,30 @@ static void run_case(int dtype, int64_t B, int64_t L, int64_t V, float T) {
     else CHECK(std::fabs(s) <= rel * sa + 1e-6, "entropy backward row %ld sums to 0", long(r));
   }
 
+  // selective log-softmax backward with the same upstream pattern: rows sum
+  // to 0, and a zero upstream gradient gives an all-zero row
+  OK(selective_log_softmax_bwd(dz_in, dtype, N, V, V, d_ids, T, d_lse2, d_gH, d_dl, V, nullptr));
+  HIP(hipDeviceSynchronize());
+  std::vector<float> ds(size_t(N * V));
+  if (dtype == GRPO_BF16) {
+    const auto raw = download(static_cast<uint16_t*>(d_dl), size_t(N * V));
+    for (size_t i = 0; i < raw.size(); ++i) ds[i] = from_bf16(raw[i]);
+  } else {
+    ds = download(static_cast<float*>(d_dl), size_t(N * V));
+  }
+  for (int64_t r = 0; r < N; ++r) {
+    double s = 0.0, sa = 0.0;
+    bool allzero = true;
+    for (int64_t j = 0; j < V; ++j) {
+      const float d = ds[size_t(r * V + j)];
+      s += d;
+      sa += std::fabs(d);
+      if (d != 0.0f) allzero = false;
+    }
+    if (gH[r] == 0.0f) CHECK(allzero, "selective backward zero row %ld", long(r));
+    else CHECK(std::fabs(s) <= rel * sa + 1e-6 && sa > 0.0, "selective backward row %ld sums to 0", long(r));
+  }
+
   for (void* ptr : {dz_in, static_cast<void*>(d_ids), static_cast<void*>(d_old),
                     static_cast<void*>(d_adv), static_cast<void*>(d_mask), static_cast<void*>(d_w),
                     static_cast<void*>(d_loss), static_cast<void*>(d_logp),
@@ -210,6 +236,82 @@ static void run_case(int dtype, int64_t B, int64_t L, int64_t V, float T) {
     HIP(hipFree(ptr));
   std::printf("case dtype=%s B=%ld L=%ld V=%ld T=%g done\n", dtype == GRPO_BF16 ? "bf16" : "f32",
               long(B), long(L), long(V), double(T));
+}
+
+// One fused-linear chunk called twice on the same inputs: the products and
+// reductions are deterministic and loss_accum / grad_weight accumulate, so the
+// second call doubles both exactly (x + x is exact in fp32); grad_hidden is
+// overwritten (identical both times) and exactly zero on rows of weight 0.
+static void run_fused() {
+  const int64_t nseq = 2, L = 8, H = 64, V = 256, N = nseq * L;
+  uint64_t seed = 777;
+  std::vector<uint16_t> h(size_t(N * H)), W(size_t(V * H));
+  for (auto& x : h) x = to_bf16(unif(seed, -1.0f, 1.0f));
+  for (auto& x : W) x = to_bf16(unif(seed, -0.1f, 0.1f));
+  std::vector<int64_t> ids(N);
+  for (auto& y : ids) y = int64_t(lcg(seed) % uint32_t(V));
+  std::vector<float> old(N), ref(N);
+  for (auto& o : old) o = -std::log(float(V)) + unif(seed, -0.3f, 0.3f);
+  for (auto& o : ref) o = -std::log(float(V)) + unif(seed, -0.1f, 0.1f);
+  const std::vector<float> adv = {0.8f, 0.0f};
+  std::vector<uint8_t> mask(N, 1);
+  for (int64_t t = L - 3; t < L; ++t) mask[L + t] = 0;
+
+  uint16_t* d_h = upload(h);
+  uint16_t* d_W = upload(W);
+  int64_t* d_ids = upload(ids);
+  float *d_old = upload(old), *d_ref = upload(ref), *d_adv = upload(adv);
+  uint8_t* d_mask = upload(mask);
+  float* d_w = dalloc<float>(N);
+  OK(grpo_loss_weights(d_mask, nseq, L, GRPO_REDUCE_TOKEN, d_w, nullptr));
+  const size_t ws = fused_linear_grpo_workspace_bytes(N, V, H);
+  CHECK(ws > 0, "workspace size");
+  void* d_ws = dalloc<uint8_t>(ws);
+  float* d_loss = dalloc<float>(1);
+  float* d_gh = dalloc<float>(size_t(N * H));
+  float* d_gW = dalloc<float>(size_t(V * H));
+  HIP(hipMemset(d_loss, 0, sizeof(float)));
+  HIP(hipMemset(d_gW, 0, size_t(V * H) * sizeof(float)));
+  grpo_params p = {0.9f, 0.04f, 0.2f, 0.28f, GRPO_TOKEN, 0};
+
+  OK(fused_linear_grpo_chunk(d_h, nseq, L, H, d_W, V, d_ids, d_old, d_ref, d_adv, d_mask, d_w,
+                             &p, d_loss, d_gh, d_gW, d_ws, ws, nullptr));
+  HIP(hipDeviceSynchronize());
+  const auto loss1 = download(d_loss, 1), gh1 = download(d_gh, size_t(N * H)),
+             gW1 = download(d_gW, size_t(V * H)), w = download(d_w, N);
+  OK(fused_linear_grpo_chunk(d_h, nseq, L, H, d_W, V, d_ids, d_old, d_ref, d_adv, d_mask, d_w,
+                             &p, d_loss, d_gh, d_gW, d_ws, ws, nullptr));
+  HIP(hipDeviceSynchronize());
+  const auto loss2 = download(d_loss, 1), gh2 = download(d_gh, size_t(N * H)),
+             gW2 = download(d_gW, size_t(V * H));
+
+  CHECK(std::isfinite(loss1[0]) && loss2[0] == 2.0f * loss1[0], "loss accumulates (%g, %g)",
+        double(loss1[0]), double(loss2[0]));
+  bool gW_ok = true, gW_nonzero = false;
+  for (size_t i = 0; i < gW1.size(); ++i) {
+    if (!std::isfinite(gW1[i]) || gW2[i] != 2.0f * gW1[i]) gW_ok = false;
+    if (gW1[i] != 0.0f) gW_nonzero = true;
+  }
+  CHECK(gW_ok, "grad_weight accumulates exactly");
+  CHECK(gW_nonzero, "grad_weight is not all zero");
+  for (int64_t r = 0; r < N; ++r) {
+    bool same = true, allzero = true;
+    for (int64_t c = 0; c < H; ++c) {
+      const float a = gh1[size_t(r * H + c)], b = gh2[size_t(r * H + c)];
+      if (!(std::isfinite(a) && a == b)) same = false;
+      if (a != 0.0f) allzero = false;
+    }
+    CHECK(same, "grad_hidden row %ld overwritten identically", long(r));
+    if (w[r] == 0.0f) CHECK(allzero, "grad_hidden row %ld of weight 0 is zero", long(r));
+  }
+  for (void* ptr : {static_cast<void*>(d_h), static_cast<void*>(d_W), static_cast<void*>(d_ids),
+                    static_cast<void*>(d_old), static_cast<void*>(d_ref),
+                    static_cast<void*>(d_adv), static_cast<void*>(d_mask),
+                    static_cast<void*>(d_w), d_ws, static_cast<void*>(d_loss),
+                    static_cast<void*>(d_gh), static_cast<void*>(d_gW)})
+    HIP(hipFree(ptr));
+  std::printf("fused chunk nseq=%ld L=%ld H=%ld V=%ld done\n", long(nseq), long(L), long(H),
+              long(V));
 }
 
 int main() {
@@ -225,6 +327,7 @@ int main() {
 
   run_case(GRPO_F32, 3, 40, 1003, 0.9f);
   run_case(GRPO_BF16, 3, 40, 4096, 1.0f);
+  run_fused();
 
   // group advantages of {1, 0, 0, 1}: +-(1/2) / (sqrt(1/3) + 1e-4)
   const std::vector<float> rw = {1, 0, 0, 1};
