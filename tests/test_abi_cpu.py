@@ -177,3 +177,24 @@ def test_gemm_logits_validation(L):
     assert call(T=0.0) == PARAM and call(T=float("nan")) == PARAM
     assert call(z=FAKE_ODD) == ALIGN
     assert call(M=1 << 30, N=1 << 30, ldz=1 << 30) == SHAPE  # grid past 31 bits
+
+
+def test_no_fallback_without_the_library():
+    """With the HIP library missing, the binding raises: no CPU path computes
+    anything in its place (and calls on CPU tensors raise as well)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import rl_fine_tuning_row_amd._lib as L, torch\n"
+        "L.LIB_PATH = '/nonexistent/libgrpo_rows.so'; L._lib = None\n"
+        "try:\n    L.lib(); print('LOADED')\n"
+        "except RuntimeError as e:\n    print('RAISED', 'not built' in str(e))\n"
+        "try:\n    out = L.entropy_from_logits(torch.zeros(2, 8)); print('COMPUTED')\n"
+        "except Exception as e:\n    print('CALL RAISED', type(e).__name__)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "RAISED True" in r.stdout and "CALL RAISED" in r.stdout, r.stdout
+    assert "LOADED" not in r.stdout and "COMPUTED" not in r.stdout
