@@ -535,7 +535,10 @@ def run_fused(args, torch, grl, synth):
     torch.cuda.synchronize()
     steps = max(1, min(args.steps, 5))
     args.steps = steps
+    base_bytes = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     ms = timed([step], steps, torch)
+    peak_bytes = torch.cuda.max_memory_allocated()
     # rows with dloss == 0 (padding) are compacted away before the products:
     # GEMM rates price the flops actually executed, on the kept rows
     kept = int((case.dloss != 0.0).sum())
@@ -550,6 +553,13 @@ def run_fused(args, torch, grl, synth):
                                  f"U{{512..1024}}",
                      "chunk_sequences": c, "workspace_bytes": ws.numel(),
                      "full_logits_fp32_bytes": case.N * case.V * 4})
+    # device memory while the batch runs: everything the caller holds (h, W,
+    # inputs, grad_hidden, grad_weight, the workspace) and nothing the library
+    # allocates; an unchunked loss would hold the batch's full logits besides
+    res["memory"] = {"allocated_bytes": base_bytes, "peak_during_batch_bytes": peak_bytes,
+                     "workspace_bytes": ws.numel(),
+                     "full_logits_bf16_bytes": case.N * case.V * 2,
+                     "full_logits_fp32_bytes": case.N * case.V * 4}
     # the dominant kernel, the logits product with its statistics epilogue,
     # timed alone on the first chunk's kept rows: back-to-back launches
     # between two events on the launch stream
