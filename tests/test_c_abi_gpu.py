@@ -16,7 +16,7 @@ BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_check")
 def test_c_abi_program():
     require_gpu()
     assert os.path.exists(BIN), "tests/c/abi_check is not built (run __graft_entry__.build())"
-    say("C ABI check program: fp32 3x40x1003 (T 0.9) and bf16 3x40x4096")
+    say("C ABI check program: fp32 3x40x1003 (T 0.9), bf16 3x40x4096, one fused-linear chunk")
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     say(r.stdout.strip())
     assert r.returncode == 0, r.stderr[-2000:]
