@@ -701,9 +701,9 @@ def run_tiny(args, torch, grl, synth):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the row pass shards by sequence with no exchange; see DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the row "
+              "pass would shard by sequence with no exchange; the fused-linear path would "
+              "all-reduce grad_weight once per step).", file=sys.stderr)
         sys.exit(2)
     import torch
     import rl_fine_tuning_row_amd as grl
