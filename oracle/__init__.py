@@ -8,6 +8,6 @@ from .grpo import (  # noqa: F401
     decode_bf16, to_f64, log_softmax_stats, selective_log_softmax,
     selective_log_softmax_bwd, entropy_from_logits, ppo_clip_terms, k3,
     grpo_forward, grpo_dlogp, dlogits_from_dlogp, grpo_backward,
-    token_mean_loss, fused_linear_grpo, fused_linear_loss,
+    fused_linear_grpo, fused_linear_loss,
     entropy_from_logits_bwd, group_advantages, loss_weights,
 )

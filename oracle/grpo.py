@@ -14,9 +14,9 @@ Sources (web pages, cited by title and section):
   (chunked LM-head input, gradients of the input chunk and of the LM-head
   weight computed during the forward and accumulated).
 * [AXOLOTL]    axolotl PR #3510 analysis, "entropy and selective log-softmax
-  with Triton kernels": section "Code analysis", part 1 (the original chunked
-  ``entropy_from_logits``) and part 2 (``selective_log_softmax`` forward and
-  custom backward).
+  with Triton kernels": section "Code analysis", part 1 (the per-row entropy
+  of the softmax, ``entropy_from_logits``) and part 2
+  (``selective_log_softmax`` forward and custom backward).
 
 Where the pages leave a step open the plain reading is taken; each such
 reading is named in the docstring of the function that takes it.
@@ -32,7 +32,10 @@ import numpy as np
 # input decoding
 # ---------------------------------------------------------------------------
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns (uint16) -> exact float64 values."""
+    """bf16 bit patterns (uint16) -> exact float64 values.
+
+    bf16 is the upper half of an IEEE binary32: the pattern shifted left by
+    16 bits is the fp32 number it stands for, exactly."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
 
@@ -81,21 +84,16 @@ def selective_log_softmax_bwd(z: np.ndarray, index: np.ndarray, grad_logp: np.nd
     return g * (onehot - p)
 
 
-def entropy_from_logits(z: np.ndarray, temperature: float = 1.0, chunk_rows: int = 128):
-    """Per-row entropy H = -sum_j p_j log p_j of softmax(z / T).
+def entropy_from_logits(z: np.ndarray, temperature: float = 1.0):
+    """Per-row entropy H = -sum_j p_j log p_j of p = softmax(z / T).
 
-    Follows the original chunked definition [AXOLOTL, "Code analysis" part 1]:
-    rows in chunks of 128, log-softmax of the chunk, then minus the row sum of
-    exp(logp) * logp.  (The chunking only bounds memory; it does not change
-    the result.)  T is 1 in that definition; a temperature divides the logits
-    first, as in the GRPO path."""
-    z = np.asarray(z, dtype=np.float64)
-    out = np.empty(z.shape[0], dtype=np.float64)
-    for r0 in range(0, z.shape[0], chunk_rows):
-        u, lse = log_softmax_stats(z[r0:r0 + chunk_rows], temperature)
-        logps = u - lse[:, None]
-        out[r0:r0 + chunk_rows] = -(np.exp(logps) * logps).sum(axis=1)
-    return out
+    [AXOLOTL, "Code analysis" part 1: the entropy of each row's softmax, from
+    its log-softmax].  T is 1 in the page's op; a temperature divides the
+    logits first, as in the GRPO path.  Written from the definition: the
+    row's log-softmax log p = u - lse, then -sum exp(log p) log p."""
+    u, lse = log_softmax_stats(z, temperature)
+    logp = u - lse[:, None]
+    return -(np.exp(logp) * logp).sum(axis=1)
 
 
 # ---------------------------------------------------------------------------
@@ -238,12 +236,6 @@ def grpo_backward(z, ids, old_logp, ref_logp, adv, mask, dloss, B, L, temperatur
     g = grpo_dlogp(fwd, ref_logp, adv, mask, dloss, B, L, beta, level)
     dz = dlogits_from_dlogp(z, ids, fwd["lse"], g, temperature)
     return dz, g, (g == 0.0)
-
-
-def token_mean_loss(loss: np.ndarray, mask) -> float:
-    """Caller-side token-mean reduction: sum m * loss / max(sum m, 1)."""
-    m = _mask01(mask, loss.size)
-    return float((m * loss).sum() / max(m.sum(), 1.0))
 
 
 # ---------------------------------------------------------------------------

@@ -566,6 +566,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
       Stat st;
       stat_init(st);
       if (nv > 0) stat_tile<64, false>(st, x, c);
+      stat_exact<false>(st, c);
       Stat o;
       o.m = __shfl_xor(st.m, 32, 64);
       o.s = __shfl_xor(st.s, 32, 64);

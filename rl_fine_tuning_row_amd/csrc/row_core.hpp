@@ -13,6 +13,16 @@
 // This is the single-read online normaliser (Milakov & Gimelshein, "Online
 // normalizer calculation for softmax", 2018) extended with the entropy sum;
 // the max is refreshed once per register tile, not per element.
+//
+// Each exponent is one FMA, fl(z c - fl(m c)): it is taken against the
+// rounded product fl(m c), not against m c itself, so while a lane streams
+// its sums hold every term scaled by 2^delta, delta = m c - fl(m c) (up to
+// half an ulp of m c: 7.6e-6 at |m c| ~ 144, i.e. T = 0.05 on logits of a few
+// units).  A max refresh rescales by 2^(fl(m_old c) - fl(m_new c)), which
+// keeps that single offset; stat_exact then removes it (delta is exact as
+// fma(m, c, -fl(m c))) before states of different lanes are merged, since
+// lse = m / T + ln s would otherwise carry delta ln 2 -- an absolute error
+// that the log-probability of a likely token (close to 0) cannot absorb.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -119,16 +129,23 @@ __device__ __forceinline__ void stat_init(Stat& st) {
 // fold a register tile of K logits into the running state
 template <int K, bool NEED_T>
 __device__ __forceinline__ void stat_tile(Stat& st, const float* x, float c) {
+  // The rescale must subtract the two ROUNDED products fl(m_old c) and
+  // fl(m_new c) -- the references the old and the new exponents were taken
+  // against.  Contracted into fma(m_old, c, -fl(m_new c)) (what HIP's default
+  // -ffp-contract=fast does to `a * c - b`) it would add m_old's offset
+  // delta to the old sums at every refresh, up to 1e-4 in log s over a row
+  // at T = 0.05.
+#pragma clang fp contract(off)
   float tm = x[0];
 #pragma unroll
   for (int k = 1; k < K; ++k) tm = fmaxf(tm, x[k]);
   const float mn = fmaxf(st.m, tm);
-  const float dl = (st.m - mn) * c;  // <= 0: rescale of the old sums
-  const float f = exp2_fast(dl);
-  if (NEED_T) st.t = f * fmaf(dl, st.s, st.t);
-  st.s = f * st.s;
-  st.m = mn;
   const float mc = mn * c;
+  const float dl = st.m * c - mc;  // <= 0: rescale of the old sums (same offset)
+  const float f = exp2_fast(dl);
+  const float t_old = NEED_T ? f * fmaf(dl, st.s, st.t) : 0.0f;
+  const float s_old = st.s;
+  st.m = mn;
   float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
   for (int k = 0; k < K; k += 2) {
@@ -143,10 +160,26 @@ __device__ __forceinline__ void stat_tile(Stat& st, const float* x, float c) {
       if (NEED_T) t1 = fmaf(e1, d1, t1);
     }
   }
-  st.s += s0 + s1;
-  if (NEED_T) st.t += t0 + t1;
+  st.s = fmaf(f, s_old, s0 + s1);
+  if (NEED_T) st.t = t_old + (t0 + t1);
 }
 
+// Re-reference a lane's sums from fl(m c) to the exact m c: every term was
+// 2^delta too large, and each t term's exponent delta too large, so
+//   s <- s 2^-delta,   t <- (t - delta s) 2^-delta.
+// delta is 0 for the empty state's products that overflow (|m c| >= 2^24
+// leaves no meaningful fraction anyway).
+template <bool NEED_T>
+__device__ __forceinline__ void stat_exact(Stat& st, float c) {
+  const float mc = st.m * c;
+  float delta = fmaf(st.m, c, -mc);
+  delta = fabsf(delta) <= 1.0f ? delta : 0.0f;
+  const float f = exp2_fast(-delta);
+  if (NEED_T) st.t = (st.t - delta * st.s) * f;
+  st.s *= f;
+}
+
+// Merge two states whose sums are referenced to their exact m c.
 template <bool NEED_T>
 __device__ __forceinline__ Stat stat_merge(const Stat& a, const Stat& b, float c) {
   const float mn = fmaxf(a.m, b.m);
@@ -181,8 +214,10 @@ __device__ __forceinline__ Stat wave_reduce_stat(Stat st, float c) {
 // holds the same bits in every wave.  (Merging all NW states in every lane
 // in turn keeps 3·NW floats and their temporaries live beside a
 // register-resident row.)
+// `st` is a lane's streamed state (sums referenced to fl(m c)).
 template <int WG, bool NEED_T>
 __device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
+  stat_exact<NEED_T>(st, c);
   st = wave_reduce_stat<NEED_T>(st, c);
   if constexpr (WG == 64) {
     return st;

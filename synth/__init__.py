@@ -6,7 +6,11 @@ random draws, fp32 -> bf16 rounding of the draws, and the layout of the
 arrays.  Quantities that need the policy's own log-probabilities (old_logp,
 ref_logp = logp + noise) are returned as *noise* here; the caller adds the
 true log-probabilities, which it takes from the oracle (tests) or from a
-stored file written by the oracle (bench).
+stored file written by the oracle (bench).  Likewise the per-token upstream
+weights ``dloss`` of a loss reduction are not formed here: a case records
+which reduction it stands for (``dloss_kind``: "mean" for the token mean,
+"sum" for the plain sum) and leaves ``dloss`` to the caller, which takes it
+from the oracle (tests) or from the library's ``grpo_loss_weights`` (bench).
 
 Every draw comes from one ``numpy.random.SeedSequence(seed)`` split into the
 named child streams of ``STREAMS`` (always in that order).  Large matrices are
@@ -117,7 +121,8 @@ class GrpoCase:
     logits: [N, V] fp32 values, or bf16 bits as uint16 (``dtype == "bf16"``).
     old_noise / ref_noise: the noise that the caller adds to the policy's own
     log-probabilities to form old_logp / ref_logp (ref_noise None: no
-    reference model, ref == policy).  dloss is the per-token upstream weight.
+    reference model, ref == policy).  dloss is the per-token upstream weight
+    (None until the caller fills it for the reduction named by dloss_kind).
     """
     name: str
     B: int
@@ -130,7 +135,7 @@ class GrpoCase:
     mask: np.ndarray
     old_noise: np.ndarray
     ref_noise: Optional[np.ndarray]
-    dloss: np.ndarray
+    dloss: Optional[np.ndarray]
     temperature: float
     beta: float
     eps_low: float
@@ -138,6 +143,7 @@ class GrpoCase:
     level: str  # "token" | "sequence"
     seed: int = 0
     sigma: float = 2.0
+    dloss_kind: str = "given"  # "mean" | "sum": dloss left to the caller
 
     @property
     def N(self) -> int:
@@ -167,13 +173,10 @@ def _mask_from_lengths(s, B, L, lo, hi):
     return (t < lens[:, None]).astype(np.uint8).reshape(-1), lens
 
 
-def token_mean_dloss(mask: np.ndarray) -> np.ndarray:
-    """Upstream per-token weight of a token-mean loss reduction, m / max(sum m, 1).
-
-    This is the caller's reduction (it sits outside the kernels); it is the
-    input recipe for the per-token ``dloss`` of the benchmarked workloads."""
-    m = mask.astype(np.float64)
-    return (m / max(m.sum(), 1.0)).astype(np.float32)
+def _kind(dloss: str) -> str:
+    if dloss not in ("mean", "sum"):
+        raise ValueError(f"dloss reduction {dloss!r} (mean or sum)")
+    return dloss
 
 
 def tiny_case(variant: str = "a", seed: int = 0, with_logits: bool = True) -> GrpoCase:
@@ -181,7 +184,7 @@ def tiny_case(variant: str = "a", seed: int = 0, with_logits: bool = True) -> Gr
 
     variant "a": as stated; "b": beta=0; "c": no reference (ref == policy);
     "s": sequence-level loss; "t": as "a" with T=0.7 (exercises 1/T).
-    The parity tests use dloss = mask (sum reduction) so dlogits is O(1)."""
+    dloss_kind "sum" (the parity tests' sum reduction, so dlogits is O(1))."""
     B, L, V = 2, 16, 1024
     s = streams(seed)
     z = normal_matrix(s["logits"], B * L, V, 2.0, bf16=False) if with_logits else None
@@ -195,9 +198,10 @@ def tiny_case(variant: str = "a", seed: int = 0, with_logits: bool = True) -> Gr
     return GrpoCase(name=f"tiny-{variant}", B=B, L=L, V=V, dtype="f32", logits=z, ids=ids,
                     adv=adv, mask=mask, old_noise=old_noise,
                     ref_noise=None if variant == "c" else ref_noise,
-                    dloss=mask.astype(np.float32), temperature=T, beta=beta,
+                    dloss=None, temperature=T, beta=beta,
                     eps_low=0.2, eps_high=0.2,
-                    level="sequence" if variant == "s" else "token", seed=seed, sigma=2.0)
+                    level="sequence" if variant == "s" else "token", seed=seed, sigma=2.0,
+                    dloss_kind="sum")
 
 
 def grpo_token_case(seed: int = 0, with_ref: bool = False, with_logits: bool = True,
@@ -210,7 +214,8 @@ def grpo_token_case(seed: int = 0, with_ref: bool = False, with_logits: bool = T
 
     At the default sizes (B=4, L=512, V=32000) this is the headline workload.
     ``with_ref`` False: no reference model (ref == policy, KL term identically
-    0); True: ref noise N(0, 0.1^2).  ``dloss``: "mean" (m / sum m) or "sum" (m)."""
+    0); True: ref noise N(0, 0.1^2).  ``dloss``: the reduction whose weights the
+    caller supplies, "mean" (token mean) or "sum"."""
     s = streams(seed)
     N = B * L
     z = normal_matrix(s["logits"], N, V, 2.0, bf16=True) if with_logits else None
@@ -221,12 +226,11 @@ def grpo_token_case(seed: int = 0, with_ref: bool = False, with_logits: bool = T
     mask, _ = _mask_from_lengths(s, B, L, lo, hi)
     old_noise = np.random.default_rng(s["old_noise"]).standard_normal(N) * 0.3
     ref_noise = np.random.default_rng(s["ref_noise"]).standard_normal(N) * 0.1
-    w = token_mean_dloss(mask) if dloss == "mean" else mask.astype(np.float32)
     return GrpoCase(name=f"grpo-token-B{B}-L{L}-V{V}" + ("-ref" if with_ref else ""),
                     B=B, L=L, V=V, dtype="bf16", logits=z, ids=ids, adv=adv, mask=mask,
                     old_noise=old_noise, ref_noise=ref_noise if with_ref else None,
-                    dloss=w, temperature=0.9, beta=0.04, eps_low=0.2, eps_high=0.28,
-                    level="token", seed=seed, sigma=2.0)
+                    dloss=None, temperature=0.9, beta=0.04, eps_low=0.2, eps_high=0.28,
+                    level="token", seed=seed, sigma=2.0, dloss_kind=_kind(dloss))
 
 
 def grpo_sequence_case(seed: int = 0, with_logits: bool = True, B: int = 8, L: int = 1024,
@@ -243,11 +247,11 @@ def grpo_sequence_case(seed: int = 0, with_logits: bool = True, B: int = 8, L: i
     mask = np.ones(N, np.uint8)
     delta = np.random.default_rng(s["old_noise"]).standard_normal(B) * 0.5
     old_noise = np.repeat(delta, L)
-    w = token_mean_dloss(mask) if dloss == "mean" else mask.astype(np.float32)
     return GrpoCase(name=f"grpo-seq-B{B}-L{L}-V{V}", B=B, L=L, V=V, dtype="bf16",
                     logits=z, ids=ids, adv=adv, mask=mask, old_noise=old_noise,
-                    ref_noise=None, dloss=w, temperature=1.0, beta=0.0, eps_low=0.2,
-                    eps_high=0.28, level="sequence", seed=seed, sigma=2.0)
+                    ref_noise=None, dloss=None, temperature=1.0, beta=0.0, eps_low=0.2,
+                    eps_high=0.28, level="sequence", seed=seed, sigma=2.0,
+                    dloss_kind=_kind(dloss))
 
 
 @dataclasses.dataclass
@@ -301,13 +305,14 @@ class FusedCase:
     mask: np.ndarray
     old_noise: np.ndarray
     ref_noise: np.ndarray
-    dloss: np.ndarray
+    dloss: Optional[np.ndarray]
     temperature: float = 0.9
     beta: float = 0.04
     eps_low: float = 0.2
     eps_high: float = 0.28
     seed: int = 0
     w_sigma: float = 0.02
+    dloss_kind: str = "given"
 
     @property
     def N(self) -> int:
@@ -325,10 +330,9 @@ def fused_case(seed: int = 0, B: int = 32, L: int = 1024, H: int = 1024, V: int 
     mask, _ = _mask_from_lengths(s, B, L, L // 2, L)
     old_noise = np.random.default_rng(s["old_noise"]).standard_normal(N) * 0.3
     ref_noise = np.random.default_rng(s["ref_noise"]).standard_normal(N) * 0.1
-    w = token_mean_dloss(mask) if dloss == "mean" else mask.astype(np.float32)
     return FusedCase(name=f"fused-B{B}-L{L}-H{H}-V{V}", B=B, L=L, H=H, V=V, hidden=h,
                      weight=W, ids=ids, adv=adv, mask=mask, old_noise=old_noise,
-                     ref_noise=ref_noise, dloss=w, seed=seed)
+                     ref_noise=ref_noise, dloss=None, seed=seed, dloss_kind=_kind(dloss))
 
 
 def add_noise_f32(logp_true: np.ndarray, noise: np.ndarray) -> np.ndarray:

@@ -15,6 +15,29 @@ RTOL, ATOL = 1e-5, 1e-6
 BF16_DZ_ATOL = 2e-2
 
 
+def bf16_dz_tol(want) -> np.ndarray:
+    """Per-element bar for bf16 dlogits: 2e-2 absolute, or one bf16 ulp of the
+    oracle's value where that is larger (|o| >= 4, where the spacing of bf16
+    numbers is 2^-5 or more, so even the correctly rounded value can sit
+    more than 2e-2 from the exact one; half an ulp is the rounding, the other
+    half the kernel's fp32 arithmetic before it)."""
+    a = np.abs(np.asarray(want, np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = np.where(a > 0, np.exp2(e - 7), 0.0)
+    return np.maximum(BF16_DZ_ATOL, ulp)
+
+
+def assert_bf16_dz(got, want, name="bf16 dlogits"):
+    err = np.abs(np.asarray(got, np.float64) - want)
+    tol = bf16_dz_tol(want)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:5]
+        raise AssertionError(f"{name}: {bad.sum()} elements over the bar; max err {err.max()}; "
+                             f"got {np.asarray(got).ravel()[i].tolist()} want {want.ravel()[i].tolist()}")
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import synth
+from case_weights import fill_dloss
 from gpu_common import bits, dev, dev_to_f64, logits_to_dev, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +36,7 @@ def _entropy_bound(z64, T, g, lse, H):
 @pytest.mark.parametrize("T", [1.0, 0.7])
 def test_entropy_bwd_fp32(T):
     lib = require_gpu()
-    c = synth.tiny_case("a")
+    c = fill_dloss(synth.tiny_case("a"))
     say(f"entropy backward fp32: rows {c.N} V {c.V} T {T}")
     z64 = c.logits.astype(np.float64)
     rng = np.random.default_rng(21)
@@ -175,7 +176,7 @@ def test_rewards_to_logits_chain():
     whose rewards are all equal get advantage 0 and their rows take the zero
     path, bit-identical to the oracle's zero-row mask."""
     lib = require_gpu()
-    c = synth.grpo_token_case(B=8, L=64, V=2048)
+    c = fill_dloss(synth.grpo_token_case(B=8, L=64, V=2048))
     say("chain: rewards -> advantages -> weights -> single-pass GRPO, B=8 L=64 V=2048")
     rewards = np.array([1, 1, 1, 1, 0, 1, 0, 0], dtype=np.float32)
     adv = lib.grpo_group_advantages(dev(rewards), 4)
@@ -205,7 +206,7 @@ def test_mask_entries_are_boolean():
     """Nonzero mask entries count as 1: a 0/2 mask gives bit-identical
     sequence-level forward and backward and loss weights."""
     lib = require_gpu()
-    c = synth.grpo_sequence_case(with_logits=False, B=4, L=64, V=2048)
+    c = fill_dloss(synth.grpo_sequence_case(with_logits=False, B=4, L=64, V=2048))
     say("mask 0/2 == mask 0/1: sequence level B4 L64 V2048, weights")
     rng = np.random.default_rng(51)
     zb = synth.f32_to_bf16_bits((rng.standard_normal((c.N, c.V)) * 2).astype(np.float32))

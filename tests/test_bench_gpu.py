@@ -1,6 +1,8 @@
 """bench.py's output line on the GPU: one JSON line with the contract's keys,
-the roofline object and (GRPO workloads) the skip A/B, for the headline and
-the tiny workload at a few steps."""
+the roofline object and (GRPO workloads) the skip A/B and the with-reference
+reading, for the headline and the tiny workload at a few steps (the other
+workloads' "configs" object is left out here: it needs minutes of input
+generation)."""
 import json
 import os
 import subprocess
@@ -21,7 +23,8 @@ def test_bench_line(workload):
     require_gpu()
     say(f"bench line: {workload}")
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload",
-                        workload, "--steps", "5", "--warmup", "2", "--no-cpu-baseline"],
+                        workload, "--steps", "5", "--warmup", "2", "--no-cpu-baseline",
+                        "--no-configs"],
                        capture_output=True, text=True, timeout=110, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
@@ -38,5 +41,7 @@ def test_bench_line(workload):
         assert d["higher_is_better"] is True and d["unit"] == "GB/s"
         ab = d["skip_ab"]
         assert ab["rounds"] == 5 and ab["skip_ms"] > 0 and ab["dense_ms"] > ab["skip_ms"]
+        wr = d["with_reference"]
+        assert wr["zero_rows"] < d["config"]["zero_rows"] and wr["single_pass"]["GB/s"] > 0
     else:
         assert d["higher_is_better"] is False and d["unit"] == "us"

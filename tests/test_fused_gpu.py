@@ -4,11 +4,27 @@ GEMM: against float64 products of the same bf16 values; the bound is the
 fp32 accumulation error, |err| <= 2 K 2^-24 sum_k |a_mk b_kn| (+ the same for
 the accumulated C).
 Fused linear: loss within 1e-5 relative (row statistics and target logit
-from the logits product's fp32 accumulators); grad_hidden and grad_weight
-within 1e-2 relative Frobenius error per tensor (the backward's softmax reads
-the logits rounded to bf16, |z| 2^-8 / T in the exponent, and dz is rounded
-to bf16, 2^-8 relative, before the two products); rows of grad_hidden whose
-dlogp is 0 are exactly 0.
+from the logits product's fp32 accumulators).  grad_hidden and grad_weight:
+every element within a bound derived from the chunk's two bf16 roundings and
+the fp32 accumulations (the backward's softmax reads z rounded to bf16, and
+dz is rounded to bf16 before the two products).  With u = 2^-24,
+p = softmax(z/T) and the oracle's dz, g, lse, logp, the error of one dz
+element is at most
+    E = |g/T| p ((2^-8 |z| + zeta) / T + e_lse + 2^-22 (1 + |z|/T))
+        + 2^-8 |dz| + (e_g / T) |onehot - p|
+where zeta = 2 H u sum_k |h_k W_k| (the logits' accumulation), e_lse =
+1e-5 |lse| + 1e-6 and e_logp = 1e-5 |logp| + 1e-6 (the forward's bar) and
+e_g = (|ratio A| [not clipped] + beta e^{ref - logp}) |dloss| e_logp (the
+coefficient's derivative in logp times that error); 2^-8 is twice bf16's
+half-ulp, 2^-22 covers the exponent's fp32 arithmetic.  Then
+    |grad_hidden[r,k] err| <= sum_j E_rj |W_jk| + 2 (V + 1) u sum_j (|dz| + E)_rj |W_jk|
+    |grad_weight[j,k] err| <= sum_r E_rj |h_rk| + 2 (N + chunks) u sum_r (|dz| + E)_rj |h_rk|
+(accumulation over V, split-K partial sums included; over the rows of every
+chunk plus one fp32 add per chunk).  Being a worst case over |.|, the bound
+is loose where a gradient cancels across rows; the relative Frobenius error
+(1e-2 per tensor, and per sampled row / vocabulary entry at the workload's
+temperature) is kept beside it.  Rows of grad_hidden whose dlogp is 0 are
+exactly 0.
 """
 import numpy as np
 import pytest
@@ -16,6 +32,7 @@ import torch
 
 import oracle
 import synth
+from case_weights import fill_dloss
 from gpu_common import dev, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -61,8 +78,9 @@ def test_gemm_layouts(a_layout, b_layout, M, N, K):
     assert (err2 <= bound + 2.0 ** -23 * np.abs(C0)).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(520, 1032, 136), (300, 264, 64), (40, 8, 8), (4096, 8200, 136)])
-def test_gemm_logits_mode(M, N, K):
+@pytest.mark.parametrize("M,N,K,T", [(520, 1032, 136, 0.9), (300, 264, 64, 0.9), (40, 8, 8, 0.9),
+                                     (4096, 8200, 136, 0.9), (520, 1032, 136, 0.05)])
+def test_gemm_logits_mode(M, N, K, T):
     """The fused chunk's logits product alone (grpo_gemm_bf16_logits): against
     float64 products of the same bf16 values, z16 within the accumulation
     bound plus bf16 rounding, every partial's max within the bound, the merged
@@ -72,10 +90,10 @@ def test_gemm_logits_mode(M, N, K):
     the last shape) the results are exact against it: z16 is the correctly
     rounded fp32 C, zy and each max are entries of C.  N = 1032 and 264 leave
     8 and 0 columns in the last 128-column half-tile, (40, 8, 8) is a single
-    tile."""
+    tile.  At T = 0.05 each partial's sum must be referenced to its exact max
+    for the merged log-sum-exp to meet its bar."""
     lib = require_gpu()
-    say(f"gemm logits mode M={M} N={N} K={K}")
-    T = 0.9
+    say(f"gemm logits mode M={M} N={N} K={K} T={T}")
     rng = np.random.default_rng(M + N + K)
     a_bits, a = _bf16(rng, (M, K))
     b_bits, b = _bf16(rng, (N, K), 0.3)
@@ -155,40 +173,110 @@ def _frob(got, want):
     return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
 
 
-@pytest.mark.parametrize("chunk,V", [(1, 392), (2, 392), (3, 392), (2, 264), (1, 8)])
-def test_fused_small_against_oracle(chunk, V):
+U = 2.0 ** -24
+
+
+def _dz_error(z, zeta, lse, g, e_g, onehot, T):
+    """Bound E on |dz_chunk - dz_exact| (module doc), with the oracle's dz;
+    rows of z are the rows of g, lse, e_g (any subset of columns)."""
+    p = np.exp(z / T - lse[:, None])
+    dz = (g / T)[:, None] * (onehot - p)
+    dz[g == 0.0] = 0.0
+    E = (np.abs(g / T)[:, None] * p *
+         ((2.0 ** -8 * np.abs(z) + zeta) / T + (1e-5 * np.abs(lse) + 1e-6)[:, None]
+          + 2.0 ** -22 * (1.0 + np.abs(z) / T))
+         + 2.0 ** -8 * np.abs(dz) + (e_g / T)[:, None] * np.abs(onehot - p))
+    E[g == 0.0] = 0.0
+    return dz, E
+
+
+def _coef_error(logp, ratio, clipped, A_row, ref, w, beta):
+    """e_g: bound on |g_chunk - g| from the forward's logp bar (module doc)."""
+    e_logp = 1e-5 * np.abs(logp) + 1e-6
+    kl = beta * np.exp(ref - logp) if ref is not None and beta != 0.0 else 0.0
+    return (np.where(clipped, 0.0, ratio * np.abs(A_row)) + kl) * np.abs(w) * e_logp
+
+
+def _assert_bound(got, want, bound, name):
+    err = np.abs(np.asarray(got, np.float64) - want)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[:4]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} elements over the bound; "
+                             f"err {err.ravel()[i].tolist()} bound {bound.ravel()[i].tolist()}")
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+
+
+def _check_fused_elementwise(case, h, W, old, ref, gh, gW, chunks):
+    """Every element of grad_hidden and grad_weight against the oracle within
+    the bound of the module doc; returns the oracle's g."""
+    T = case.temperature
+    z = h @ W.T
+    ref64 = ref.astype(np.float64)
+    fwd = oracle.grpo_forward(z, case.ids, old.astype(np.float64), ref64, case.adv, case.mask,
+                              case.B, case.L, T, case.beta, case.eps_low, case.eps_high)
+    g = oracle.grpo_dlogp(fwd, ref64, case.adv, case.mask, case.dloss, case.B, case.L, case.beta)
+    A_row = np.repeat(case.adv.astype(np.float64), case.L)
+    e_g = _coef_error(fwd["logp"], fwd["ratio"], fwd["is_clipped"], A_row, ref64,
+                      case.dloss.astype(np.float64), case.beta)
+    zeta = 2 * case.H * U * (np.abs(h) @ np.abs(W).T)
+    onehot = np.zeros_like(z)
+    onehot[np.arange(case.N), case.ids] = 1.0
+    dz, E = _dz_error(z, zeta, fwd["lse"], g, e_g, onehot, T)
+    aW, ah = np.abs(W), np.abs(h)
+    gh_o, gW_o = dz @ W, dz.T @ h
+    bh = E @ aW + 2 * (case.V + 1) * U * ((np.abs(dz) + E) @ aW)
+    bW = E.T @ ah + 2 * (case.N + chunks) * U * ((np.abs(dz) + E).T @ ah)
+    rh = _assert_bound(gh, gh_o, bh, "grad_hidden")
+    rW = _assert_bound(gW, gW_o, bW, "grad_weight")
+    say(f"  largest error / bound: grad_hidden {rh:.3f}, grad_weight {rW:.3f}; Frobenius "
+        f"{_frob(gh, gh_o):.2e}, {_frob(gW, gW_o):.2e}")
+    # the summary bar holds where |z|/T is moderate (the workloads' T = 0.9);
+    # at T = 0.1 or below the bf16 z in the backward's softmax moves p by up to
+    # |z| 2^-9 / T, a few percent, and only the element bound applies
+    if T >= 0.5:
+        assert _frob(gh, gh_o) <= 1e-2 and _frob(gW, gW_o) <= 1e-2
+    return g
+
+
+@pytest.mark.parametrize("chunk,V,T", [(1, 392, 0.9), (2, 392, 0.9), (3, 392, 0.9),
+                                       (2, 264, 0.9), (1, 8, 0.9), (2, 392, 0.1),
+                                       (3, 264, 0.05)])
+def test_fused_small_against_oracle(chunk, V, T):
     """V = 392 leaves 8 columns in the last 128-column half-tile of the
     logits product, V = 264 leaves one half-tile empty, V = 8 has one tile
     with 8 columns: the partial statistics of those must fold exactly the
-    columns inside V."""
+    columns inside V.  At T = 0.1 and 0.05 every other row samples its most
+    likely token, so logp is close to 0 and its 1e-6 floor binds: the
+    statistics' sums must be referenced to the exact max, not to its rounded
+    product with log2(e)/T."""
     lib = require_gpu()
-    case = synth.fused_case(B=5, L=24, H=128, V=V, dloss="sum")
-    say(f"fused-linear small: B={case.B} L={case.L} H={case.H} V={case.V} chunk={chunk}")
+    case = fill_dloss(synth.fused_case(B=5, L=24, H=128, V=V, dloss="sum"))
     h = oracle.decode_bf16(case.hidden)
-    W = oracle.decode_bf16(case.weight) * 1.0
+    W = oracle.decode_bf16(case.weight)
+    if T != 0.9:
+        case.temperature = T
+        ids = case.ids.copy()
+        ids[::2] = (h @ W.T)[::2].argmax(axis=1)
+        case.ids = ids
+    say(f"fused-linear small: B={case.B} L={case.L} H={case.H} V={case.V} chunk={chunk} T={T}")
     logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
     old, ref = _fused_inputs(case, logp_true)
     loss, gh, gW = _run_fused(lib, case, old, ref, chunk)
-    l_o, gh_o, gW_o = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
-                                               ref.astype(np.float64), case.adv, case.mask,
-                                               case.dloss, case.B, case.L, case.temperature,
-                                               case.beta, case.eps_low, case.eps_high, chunk)
+    l_o, _, _ = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
+                                         ref.astype(np.float64), case.adv, case.mask,
+                                         case.dloss, case.B, case.L, case.temperature,
+                                         case.beta, case.eps_low, case.eps_high, chunk)
     assert abs(loss - l_o) <= 1e-5 * abs(l_o) + 1e-6, (loss, l_o)
-    assert _frob(gh, gh_o) <= 1e-2, _frob(gh, gh_o)
-    assert _frob(gW.cpu().numpy(), gW_o) <= 1e-2
+    chunks = (case.B + chunk - 1) // chunk
+    g = _check_fused_elementwise(case, h, W, old, ref, gh, gW.cpu().numpy(), chunks)
     # rows with dlogp == 0 give exactly zero grad_hidden
-    z = h @ W.T
-    fwd = oracle.grpo_forward(z, case.ids, old.astype(np.float64), ref.astype(np.float64),
-                              case.adv, case.mask, case.B, case.L, case.temperature, case.beta,
-                              case.eps_low, case.eps_high)
-    g = oracle.grpo_dlogp(fwd, ref.astype(np.float64), case.adv, case.mask, case.dloss, case.B,
-                          case.L, case.beta)
     assert (gh[g == 0.0] == 0.0).all()
 
 
 def test_fused_deterministic():
     lib = require_gpu()
-    case = synth.fused_case(B=4, L=32, H=128, V=512, dloss="mean")
+    case = fill_dloss(synth.fused_case(B=4, L=32, H=128, V=512, dloss="mean"))
     say("fused-linear determinism")
     h = oracle.decode_bf16(case.hidden)
     W = oracle.decode_bf16(case.weight)
@@ -205,7 +293,7 @@ def test_fused_on_a_side_stream_of_the_caller():
     after chunk with no host synchronisation between them, every output is
     bit-identical to the default-stream run."""
     lib = require_gpu()
-    case = synth.fused_case(B=6, L=40, H=128, V=1032, dloss="mean")
+    case = fill_dloss(synth.fused_case(B=6, L=40, H=128, V=1032, dloss="mean"))
     say("fused-linear on a non-default caller stream")
     h = oracle.decode_bf16(case.hidden)
     W = oracle.decode_bf16(case.weight)
@@ -224,7 +312,7 @@ def test_fused_full_size(chunk):
     stored logp; sampled rows of grad_hidden and sampled vocabulary rows of
     grad_weight against the oracle computed one by one."""
     lib = require_gpu()
-    case = synth.fused_case(dloss="mean")
+    case = fill_dloss(synth.fused_case(dloss="mean"))
     say(f"fused-linear full size: B32 L1024 H1024 V151936, chunk {chunk} sequences")
     rows = synth.stored_check_rows("fused")
     logp_true = synth.load_stored_logp("fused", case.hidden[rows])
@@ -247,34 +335,44 @@ def test_fused_full_size(chunk):
     h = oracle.decode_bf16(case.hidden)
     W = oracle.decode_bf16(case.weight)
     T = case.temperature
+    chunks = (case.B + chunk - 1) // chunk
+    e_g = _coef_error(logp_true, ratio, clipped, A_row, ref.astype(np.float64),
+                      case.dloss.astype(np.float64), case.beta)
+    aW, ah = np.abs(W), np.abs(h)
     rng = np.random.default_rng(5)
-    # grad_hidden rows
+    worst = [0.0, 0.0]
+    # grad_hidden rows: every element within the bound (module doc)
     rsel = np.concatenate([rng.choice(np.flatnonzero(g != 0.0), 6, replace=False), [0, N - 1]])
     for r in rsel:
-        zr = W @ h[r]
-        p = np.exp(zr / T - lse_true[r])
-        dz = -(g[r] / T) * p
-        dz[case.ids[r]] += g[r] / T
-        want = dz @ W
+        zr = (W @ h[r])[None, :]
+        zeta = 2 * case.H * U * (aW @ ah[r])[None, :]
+        oh = np.zeros_like(zr)
+        oh[0, case.ids[r]] = 1.0
+        dz, E = _dz_error(zr, zeta, lse_true[r:r + 1], g[r:r + 1], e_g[r:r + 1], oh, T)
+        want = (dz @ W)[0]
+        bound = (E @ aW + 2 * (case.V + 1) * U * ((np.abs(dz) + E) @ aW))[0]
+        worst[0] = max(worst[0], _assert_bound(gh[r], want, bound, f"grad_hidden row {r}"))
         assert _frob(gh[r], want) <= 1e-2, (r, _frob(gh[r], want))
     # grad_weight rows (vocabulary entries), including sampled-token entries
     vsel = np.concatenate([rng.integers(0, case.V, 4), case.ids[rsel[:4]]])
     gWn = gW[torch.from_numpy(vsel).cuda()].cpu().numpy()
     for k, v in enumerate(vsel):
-        zv = h @ W[v]
-        p = np.exp(zv / T - lse_true)
-        dzv = -(g / T) * p
-        hit = case.ids == v
-        dzv[hit] += g[hit] / T
-        want = dzv @ h
+        zv = (h @ W[v])[:, None]
+        zeta = 2 * case.H * U * (ah @ aW[v])[:, None]
+        oh = (case.ids == v).astype(np.float64)[:, None]
+        dz, E = _dz_error(zv, zeta, lse_true, g, e_g, oh, T)
+        want = (dz.T @ h)[0]
+        bound = (E.T @ ah + 2 * (N + chunks) * U * ((np.abs(dz) + E).T @ ah))[0]
+        worst[1] = max(worst[1], _assert_bound(gWn[k], want, bound, f"grad_weight entry {v}"))
         assert _frob(gWn[k], want) <= 1e-2, (v, _frob(gWn[k], want))
+    say(f"  largest error / bound on the sampled rows {worst[0]:.3f}, entries {worst[1]:.3f}")
 
 
 def _fused_case_with_gaps(B=4, L=40, H=128, V=392):
     """Small case whose weights are 0 on trailing padding and also on rows in
     the middle of sequences (every third valid token) and on the first token
     of sequence 1."""
-    case = synth.fused_case(B=B, L=L, H=H, V=V, dloss="sum")
+    case = fill_dloss(synth.fused_case(B=B, L=L, H=H, V=V, dloss="sum"))
     w = case.dloss.copy()
     valid = np.flatnonzero(w != 0.0)
     w[valid[::3]] = 0.0
@@ -297,20 +395,22 @@ def test_fused_skips_zero_weight_rows(chunk):
     W = oracle.decode_bf16(case.weight)
     logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
     old, ref = _fused_inputs(case, logp_true)
-    l_o, gh_o, gW_o = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
-                                               ref.astype(np.float64), case.adv, case.mask,
-                                               case.dloss, case.B, case.L, case.temperature,
-                                               case.beta, case.eps_low, case.eps_high, chunk)
+    l_o, _, _ = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
+                                         ref.astype(np.float64), case.adv, case.mask,
+                                         case.dloss, case.B, case.L, case.temperature,
+                                         case.beta, case.eps_low, case.eps_high, chunk)
     dropped = np.flatnonzero(case.dloss == 0.0)
     poisoned_old = old.copy()
     poisoned_old[dropped[0]] = np.nan
+    ids_clean = case.ids
     ids_bad = case.ids.copy()
     ids_bad[dropped[1]] = case.V + 7
     case.ids = ids_bad
     loss, gh, gW = _run_fused(lib, case, poisoned_old, ref, chunk)
+    case.ids = ids_clean
     assert np.isfinite(loss) and abs(loss - l_o) <= 1e-5 * abs(l_o) + 1e-6, (loss, l_o)
-    assert _frob(gh, gh_o) <= 1e-2, _frob(gh, gh_o)
-    assert _frob(gW.cpu().numpy(), gW_o) <= 1e-2
+    chunks = (case.B + chunk - 1) // chunk
+    _check_fused_elementwise(case, h, W, old, ref, gh, gW.cpu().numpy(), chunks)
     assert (gh[dropped] == 0.0).all()
 
 
@@ -321,7 +421,7 @@ def test_fused_invalid_id_on_a_kept_row(bad):
     row's grad_hidden is NaN and (as a sum over rows) every entry of
     grad_weight is NaN; every other row of grad_hidden is unaffected."""
     lib = require_gpu()
-    case = synth.fused_case(B=3, L=24, H=128, V=264, dloss="sum")
+    case = fill_dloss(synth.fused_case(B=3, L=24, H=128, V=264, dloss="sum"))
     h = oracle.decode_bf16(case.hidden)
     W = oracle.decode_bf16(case.weight)
     logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
@@ -346,7 +446,7 @@ def test_fused_all_rows_zero_weight():
     """A chunk whose weights are all 0 leaves loss_accum and grad_weight as they
     were (bit for bit) and writes grad_hidden = 0."""
     lib = require_gpu()
-    case = synth.fused_case(B=2, L=16, H=64, V=256, dloss="sum")
+    case = fill_dloss(synth.fused_case(B=2, L=16, H=64, V=256, dloss="sum"))
     say("fused-linear chunk with every weight 0")
     T = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
              eps_high=case.eps_high)

@@ -21,6 +21,7 @@ import scipy.stats
 
 import oracle
 import synth
+from case_weights import fill_dloss
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
 
@@ -28,6 +29,32 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
 def _gold():
     with open(GOLDEN) as f:
         return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# input decoding
+# ---------------------------------------------------------------------------
+def test_decode_bf16_every_pattern_matches_torch():
+    """All 65536 bf16 bit patterns decode to the value torch's bfloat16 ->
+    float32 conversion gives (NaN patterns to NaN)."""
+    import torch
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_bf16(pat)
+    ref = torch.from_numpy(pat.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # sign of zero kept
+    assert np.signbit(ours[0x8000]) and not np.signbit(ours[0x0000])
+
+
+def test_decode_bf16_hand_values():
+    """Patterns whose values follow from the binary32 layout by hand."""
+    pats = np.array([0x3F80, 0xBF80, 0x4049, 0x4000, 0x3F00, 0x0001, 0x0080, 0x7F80, 0xFF80,
+                     0x7F7F, 0x3F81], np.uint16)
+    want = [1.0, -1.0, 3.140625, 2.0, 0.5, 2.0 ** -133, 2.0 ** -126, np.inf, -np.inf,
+            (2 - 2 ** -7) * 2.0 ** 127, 1 + 2 ** -7]
+    assert oracle.decode_bf16(pats).tolist() == want
 
 
 # ---------------------------------------------------------------------------
@@ -47,7 +74,7 @@ def test_lse_matches_scipy(T):
 @pytest.mark.parametrize("T", [1.0, 0.9])
 def test_entropy_matches_scipy(T):
     rng = np.random.default_rng(2)
-    z = rng.standard_normal((300, 257)) * 2.0   # > 2 chunks of 128 rows, ragged tail
+    z = rng.standard_normal((300, 257)) * 2.0
     H = oracle.entropy_from_logits(z, T)
     p = scipy.special.softmax(z / T, axis=1)
     np.testing.assert_allclose(H, scipy.stats.entropy(p, axis=1), rtol=1e-12)
@@ -162,7 +189,7 @@ def test_k3_properties():
 
 
 def _tiny_inputs(variant):
-    case = synth.tiny_case(variant)
+    case = fill_dloss(synth.tiny_case(variant))
     z = case.logits.astype(np.float64)
     logp_true, _ = oracle.selective_log_softmax(z, case.ids, case.temperature)
     old = synth.add_noise_f32(logp_true, case.old_noise).astype(np.float64)
@@ -295,7 +322,7 @@ def test_selective_logsoftmax_bwd_finite_differences():
 
 def _fused_tiny():
     B, L, H, V = 2, 4, 16, 64
-    case = synth.fused_case(B=B, L=L, H=H, V=V, dloss="sum")
+    case = fill_dloss(synth.fused_case(B=B, L=L, H=H, V=V, dloss="sum"))
     h = oracle.decode_bf16(case.hidden)
     W = oracle.decode_bf16(case.weight) * 25.0   # logits O(1) so the ratios move
     T = case.temperature

@@ -7,7 +7,9 @@ Tolerances:
   * is_clipped: exact, except where the oracle's log-ratio lies within the
     forward tolerance of a clip boundary (there the row is compared against
     the branch the GPU took);
-  * bf16 dlogits: 2e-2 absolute;
+  * bf16 dlogits: 2e-2 absolute, or one bf16 ulp of the oracle value where
+    that is larger (|o| >= 4, reached with sum-reduction weights at low
+    temperature: |g/T| = 20 at T = 0.05);
   * fp32 dlogits: the forward tolerance carried through the backward formula.
     With e_logp = 1e-5|logp| + 1e-6 and e_lse = 1e-5|lse| + 1e-6 (the bounds
     the forward meets), the row coefficient g/T moves by at most
@@ -26,7 +28,8 @@ import torch
 
 import oracle
 import synth
-from gpu_common import (BF16_DZ_ATOL, GrpoInputs, assert_rel, bits, dev, dev_to_f64,
+from case_weights import fill_dloss
+from gpu_common import (GrpoInputs, assert_bf16_dz, assert_rel, bits, dev, dev_to_f64,
                         kink_distance, logits_to_dev, require_gpu, run_grpo_gpu, say)
 
 pytestmark = pytest.mark.gpu
@@ -57,13 +60,35 @@ def oracle_expectations(inp: GrpoInputs, z64, fwd_gpu, logp_all=None):
     return o, g
 
 
-def check_forward(c, o, fwd, logits_bits=None):
-    rows = c.N
+def logp_slopes(c, o, ref):
+    """|d kl / d logp| and |d loss / d logp| per row, and the logp error bar
+    e_logp = 1e-5 |logp| + 1e-6 they carry into kl and the loss (module doc):
+    kl = e^d - d - 1 with d = ref - logp moves by |e^d - 1| e_logp; the loss
+    by |ratio A| [not clipped] e_logp + beta |e^d - 1| e_logp (at sequence
+    level the ratio term takes the largest e_logp of the sequence, the bar of
+    its mean log-ratio)."""
+    logp = o["logp"]
+    e = 1e-5 * np.abs(logp) + 1e-6
+    kl_s = np.abs(np.expm1(ref - logp)) if ref is not None else np.zeros_like(logp)
+    A = np.abs(np.repeat(np.asarray(c.adv, np.float64), c.L))
+    if c.level == "token":
+        pg = np.where(o["is_clipped"], 0.0, o["ratio"] * A) * e
+    else:
+        e_seq = np.repeat(e.reshape(c.B, c.L).max(1), c.L)
+        pg = np.where(o["is_clipped"], 0.0, np.repeat(o["seq_ratio"], c.L) * A) * e_seq
+    return kl_s * e, pg + c.beta * kl_s * e
+
+
+def check_forward(c, o, fwd, logits_bits=None, ref=None):
+    """Per-row outputs against the oracle: logp, lse, entropy at 1e-5 |o| + 1e-6;
+    kl and the loss, computed from logp, also within what logp's own bar
+    carries into them (logp_slopes)."""
     assert_rel(fwd["logp"].cpu().numpy(), o["logp"], "logp")
     assert_rel(fwd["lse"].cpu().numpy(), o["lse"], "lse")
     assert_rel(fwd["entropy"].cpu().numpy(), o["entropy"], "entropy")
-    assert_rel(fwd["kl"].cpu().numpy(), o["kl"], "kl")
-    assert_rel(fwd["loss"].cpu().numpy(), o["loss"], "loss")
+    e_kl, e_loss = logp_slopes(c, o, ref)
+    assert_rel(fwd["kl"].cpu().numpy(), o["kl"], "kl", atol=1e-6 + e_kl)
+    assert_rel(fwd["loss"].cpu().numpy(), o["loss"], "loss", atol=1e-6 + e_loss)
     if fwd.get("gathered") is not None:
         g = fwd["gathered"].cpu().numpy()
         assert np.array_equal(g.astype(np.float64), o["gathered"]), "gathered not bit-exact"
@@ -104,8 +129,7 @@ def check_backward(c, o, g, dz, zr, z64, inp):
     assert (b[zero_exp] == 0).all(), "zero rows are not +0.0"
     coef = g / c.temperature
     if dz.dtype == torch.bfloat16:
-        err = np.abs(got - dz_o).max()
-        assert err <= BF16_DZ_ATOL, f"bf16 dlogits max err {err}"
+        assert_bf16_dz(got, dz_o)
     else:
         tol = coef_error_bound(c, inp, o, o["logp"]) + np.abs(coef) * (1e-5 * np.abs(o["lse"]) + 2e-6)
         err = np.abs(got - dz_o)
@@ -116,7 +140,7 @@ def check_backward(c, o, g, dz, zr, z64, inp):
 
 
 def _tiny(variant):
-    case = synth.tiny_case(variant)
+    case = fill_dloss(synth.tiny_case(variant))
     z64 = case.logits.astype(np.float64)
     logp_true, _ = oracle.selective_log_softmax(z64, case.ids, case.temperature)
     return case, z64, GrpoInputs(case, logp_true)
@@ -132,7 +156,7 @@ def test_tiny_grpo_parity(variant):
     say(f"tiny GRPO parity: variant {variant}, B={case.B} L={case.L} V={case.V} fp32, seed 0")
     fwd, dz, zr = run_grpo_gpu(lib, logits_to_dev(case.logits, "f32"), inp)
     o, g = oracle_expectations(inp, z64, fwd)
-    check_forward(case, o, fwd)
+    check_forward(case, o, fwd, ref=inp.ref)
     check_backward(case, o, g, dz, zr, z64, inp)
     if variant in ("b", "c"):
         # zero-advantage sequence: exactly zero rows
@@ -156,7 +180,7 @@ def test_tiny_skip_equals_dense(variant):
 # headline token-level case: B=4, L=512, V=32000, bf16
 # ---------------------------------------------------------------------------
 def _token_case(with_ref, dloss):
-    case = synth.grpo_token_case(with_ref=with_ref, dloss=dloss)
+    case = fill_dloss(synth.grpo_token_case(with_ref=with_ref, dloss=dloss))
     logp = synth.load_stored_logp("token", case.logits[synth.stored_check_rows("token")])
     return case, GrpoInputs(case, logp)
 
@@ -171,7 +195,7 @@ def test_token_level_parity(with_ref, dloss):
     fwd, dz, zr = run_grpo_gpu(lib, t, inp)
     z64 = oracle.decode_bf16(case.logits)
     o, g = oracle_expectations(inp, z64, fwd)
-    check_forward(case, o, fwd)
+    check_forward(case, o, fwd, ref=inp.ref)
     check_backward(case, o, g, dz, zr, z64, inp)
     say(f"  zero rows: {int(zr.sum())} of {case.N}; clipped: {int(fwd['is_clipped'].sum())}")
     # skip vs forced dense on the same inputs
@@ -208,12 +232,84 @@ def bits_t(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
+def test_token_level_inputs_unchanged_and_row_outputs_guarded():
+    """No call writes to its inputs (logits, ids, old_logp, ref_logp, adv,
+    mask, dloss, and the backward's logp / lse stay bit-identical), and the
+    per-row outputs of the forward, the backward and the single pass write
+    exactly their B*L entries: NaN guard bands of 64 entries on either side
+    of every output buffer stay untouched."""
+    lib = require_gpu()
+    case, inp = _token_case(True, "sum")
+    say("token-level canaries: inputs bit-unchanged, guard bands around per-row outputs")
+    t = logits_to_dev(case.logits, "bf16")
+    d = inp.to_dev()
+    N, G = case.N, 64
+    kw = dict(temperature=case.temperature, beta=case.beta, eps_low=case.eps_low,
+              eps_high=case.eps_high)
+
+    def guarded(dtype):
+        # the returned full buffer is the bit view the guards are compared on
+        # (NaN != NaN for torch.equal on floats)
+        if dtype == torch.float32:
+            full = torch.full((N + 2 * G,), float("nan"), dtype=dtype, device="cuda")
+            return full.view(torch.int32), full[G:G + N]
+        full = torch.full((N + 2 * G,), 0xA5, dtype=dtype, device="cuda")
+        return full, full[G:G + N]
+
+    def snap(ts):
+        return [x.clone() for x in ts]
+
+    inputs = [t.view(torch.int16), d["ids"], d["old_logp"], d["ref_logp"], d["adv"], d["mask"],
+              d["dloss"]]
+    before = snap(inputs)
+    fulls, out = {}, {}
+    for k in ("loss", "logp", "lse", "entropy", "kl", "gathered"):
+        fulls[k], out[k] = guarded(torch.float32)
+    fulls["is_clipped"], out["is_clipped"] = guarded(torch.uint8)
+    guards = {k: (v[:G].clone(), v[G + N:].clone()) for k, v in fulls.items()}
+    fwd = lib.grpo_logits_fwd(t, d["ids"], d["old_logp"], d["adv"], case.B, case.L,
+                              ref_logp=d["ref_logp"], mask=d["mask"], out=out, gathered=True, **kw)
+    logp_lse = snap([fwd["logp"], fwd["lse"]])
+    zfull, zr = guarded(torch.uint8)
+    zguard = (zfull[:G].clone(), zfull[G + N:].clone())
+    lib.grpo_logits_bwd(t, d["ids"], d["old_logp"], d["adv"], case.B, case.L, fwd["logp"],
+                        fwd["lse"], d["dloss"], ref_logp=d["ref_logp"], mask=d["mask"],
+                        zero_row=zr, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(inputs + [fwd["logp"], fwd["lse"]], before + logp_lse):
+        assert torch.equal(a, b)
+    # the single pass into fresh guarded buffers
+    fulls1, out1 = {}, {}
+    for k in ("loss", "logp", "lse", "entropy", "kl"):
+        fulls1[k], out1[k] = guarded(torch.float32)
+    fulls1["is_clipped"], out1["is_clipped"] = guarded(torch.uint8)
+    guards1 = {k: (v[:G].clone(), v[G + N:].clone()) for k, v in fulls1.items()}
+    z1full, zr1 = guarded(torch.uint8)
+    z1guard = (z1full[:G].clone(), z1full[G + N:].clone())
+    lib.grpo_logits_fwd_bwd(t, d["ids"], d["old_logp"], d["adv"], case.B, case.L, d["dloss"],
+                            ref_logp=d["ref_logp"], mask=d["mask"], out=out1, zero_row=zr1, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(inputs, before):
+        assert torch.equal(a, b)
+    for fs, gs in ((fulls, guards), (fulls1, guards1)):
+        for k, v in fs.items():
+            lo, hi = gs[k]
+            assert torch.equal(v[:G], lo) and torch.equal(v[G + N:], hi), f"{k} guard band written"
+    for full, (lo, hi) in ((zfull, zguard), (z1full, z1guard)):
+        assert torch.equal(full[:G], lo) and torch.equal(full[G + N:], hi), "zero_row guard band"
+    # the guarded outputs hold the same values as unguarded runs
+    ref_fwd, _, ref_zr = run_grpo_gpu(lib, t, inp)
+    for k in ("loss", "logp", "lse", "entropy", "kl", "is_clipped"):
+        assert torch.equal(out[k], ref_fwd[k]), k
+    assert torch.equal(zr, ref_zr) and torch.equal(zr1, ref_zr)
+
+
 # ---------------------------------------------------------------------------
 # sequence-level case: B=8, L=1024, V=151936, bf16, beta = 0
 # ---------------------------------------------------------------------------
 def test_sequence_level_parity():
     lib = require_gpu()
-    case = synth.grpo_sequence_case(dloss="sum")
+    case = fill_dloss(synth.grpo_sequence_case(dloss="sum"))
     logp_true = synth.load_stored_logp("sequence", case.logits[synth.stored_check_rows("sequence")])
     inp = GrpoInputs(case, logp_true)
     say("sequence-level GRPO parity: B8 L1024 V151936 bf16, beta 0")
@@ -247,7 +343,7 @@ def test_sequence_level_parity():
     assert_rel(fwd["entropy"].cpu().numpy()[rows], oracle.entropy_from_logits(z64), "entropy (sampled)")
     dz_o = oracle.dlogits_from_dlogp(z64, case.ids[rows], lse, g[rows], case.temperature)
     got = dev_to_f64(dz[torch.from_numpy(rows).cuda()])
-    assert np.abs(got - dz_o).max() <= BF16_DZ_ATOL
+    assert_bf16_dz(got, dz_o)
     # every row: zero rows +0.0, row sums ~ 0
     zb = dz[torch.from_numpy(zr_np).cuda()].view(torch.int16)
     assert int((zb != 0).sum()) == 0
@@ -280,7 +376,7 @@ def test_entropy_and_selective_logsoftmax_full():
     assert_rel(logp.cpu().numpy()[rows], lp_o, "logp (sampled)")
     assert_rel(lse.cpu().numpy()[rows], lse_o, "lse (sampled)")
     dz_o = oracle.selective_log_softmax_bwd(z64, case.ids[rows], case.grad[rows])
-    assert np.abs(dev_to_f64(dz[torch.from_numpy(rows).cuda()]) - dz_o).max() <= BF16_DZ_ATOL
+    assert_bf16_dz(dev_to_f64(dz[torch.from_numpy(rows).cuda()]), dz_o)
     # every row: bounds and row sums
     Hn = H.cpu().numpy()
     assert (Hn >= -1e-6).all() and (Hn <= math.log(case.V) * (1 + 1e-6)).all()
@@ -333,10 +429,62 @@ def test_ragged_and_strided_rows(dtype, V, ld_extra):
     inp = GrpoInputs(case, lp)
     fwd, dz, zr = run_grpo_gpu(lib, t, inp)
     o, g = oracle_expectations(inp, z64, fwd)
-    check_forward(case, o, fwd)
+    check_forward(case, o, fwd, ref=inp.ref)
     check_backward(case, o, g, dz, zr, z64, inp)
     H = lib.entropy_from_logits(t, temperature=0.9)
     assert_rel(H.cpu().numpy(), oracle.entropy_from_logits(z64, 0.9), "entropy")
+
+
+@pytest.mark.parametrize("dtype,V,ld_extra", [("f32", 17, 0), ("bf16", 1003, 0), ("bf16", 1003, 1),
+                                             ("bf16", 32000, 0), ("f32", 4099, 5),
+                                             ("bf16", 151936, 0)])
+@pytest.mark.parametrize("T", [0.05, 0.1])
+def test_low_temperature_rows(dtype, V, ld_extra, T):
+    """T = 0.05 and 0.1 with every other row sampling its most likely token,
+    so logp is close to 0 and the 1e-6 floor of the bar binds: the GRPO
+    forward and backward (two passes), the entropy, and the selective
+    log-softmax forward and backward.  A lane's sums must be referenced to
+    its exact max: referenced to the rounded product fl(m log2e / T) they
+    carry an offset of up to half an ulp of it (7.6e-6 at m/T ~ 100), which
+    lse and logp inherit.  bf16 dlogits reach |o| >= 4 here, where the bar is
+    one bf16 ulp of the oracle value."""
+    lib = require_gpu()
+    say(f"low temperature: dtype {dtype} V={V} ld=V+{ld_extra} T={T}")
+    B, L = 2, 4
+    rng = np.random.default_rng(V + 7 * ld_extra + int(100 * T))
+    zf = (rng.standard_normal((B * L, V + ld_extra)) * 2.0).astype(np.float32)
+    zb = synth.f32_to_bf16_bits(zf) if dtype == "bf16" else zf
+    t = logits_to_dev(zb, dtype)[:, :V]
+    z64 = oracle.to_f64(zb, dtype)[:, :V]
+    ids = rng.integers(0, V, B * L).astype(np.int64)
+    ids[::2] = z64[::2].argmax(axis=1)
+    lp, _ = oracle.selective_log_softmax(z64, ids, T)
+    case = synth.GrpoCase(name="low-T", B=B, L=L, V=V, dtype=dtype, logits=None, ids=ids,
+                          adv=np.array([0.7, -1.2], np.float32), mask=np.ones(B * L, np.uint8),
+                          old_noise=rng.standard_normal(B * L) * 0.2,
+                          ref_noise=rng.standard_normal(B * L) * 0.1,
+                          dloss=np.ones(B * L, np.float32), temperature=T, beta=0.04,
+                          eps_low=0.2, eps_high=0.28, level="token")
+    inp = GrpoInputs(case, lp)
+    fwd, dz, zr = run_grpo_gpu(lib, t, inp)
+    o, g = oracle_expectations(inp, z64, fwd)
+    check_forward(case, o, fwd, ref=inp.ref)
+    check_backward(case, o, g, dz, zr, z64, inp)
+    H = lib.entropy_from_logits(t, temperature=T)
+    lpg, lseg = lib.selective_log_softmax(t, dev(ids), temperature=T)
+    gr = rng.standard_normal(B * L).astype(np.float32)
+    dzs = lib.selective_log_softmax_bwd(t, dev(ids), lseg, dev(gr), temperature=T)
+    torch.cuda.synchronize()
+    lp_o, lse_o = oracle.selective_log_softmax(z64, ids, T)
+    assert_rel(H.cpu().numpy(), oracle.entropy_from_logits(z64, T), "entropy")
+    assert_rel(lpg.cpu().numpy(), lp_o, "selective logp")
+    assert_rel(lseg.cpu().numpy(), lse_o, "selective lse")
+    dzs_o = oracle.selective_log_softmax_bwd(z64, ids, gr, T)
+    if dtype == "bf16":
+        assert_bf16_dz(dev_to_f64(dzs), dzs_o, "selective dlogits")
+    else:
+        tol = np.abs(gr / T)[:, None] * (1e-5 * np.abs(lse_o) + 2e-6)[:, None]
+        assert (np.abs(dev_to_f64(dzs) - dzs_o) <= tol).all(), "selective fp32 dlogits"
 
 
 def test_empty_rows_are_noop():
@@ -425,7 +573,7 @@ def test_sequence_level_partial_masks(with_ref):
     inp = GrpoInputs(case, lp)
     fwd, dz, zr = run_grpo_gpu(lib, logits_to_dev(z, "f32"), inp)
     o, g = oracle_expectations(inp, z64, fwd)
-    check_forward(case, o, fwd)
+    check_forward(case, o, fwd, ref=inp.ref)
     check_backward(case, o, g, dz, zr, z64, inp)
     # the empty sequence (and the masked tail of the others) carries no
     # policy gradient; without a reference model its rows are exactly zero

@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import synth
+from case_weights import fill_dloss
 
 
 def test_bf16_rounding_matches_torch():
@@ -30,17 +31,17 @@ def test_blocked_matrix_rows_and_determinism():
 
 
 def test_tiny_case_structure():
-    c = synth.tiny_case("a")
+    c = fill_dloss(synth.tiny_case("a"))
     assert c.logits.shape == (32, 1024) and c.logits.dtype == np.float32
     assert c.adv[1] == 0.0 and c.adv[0] != 0.0
     assert c.mask.all() and c.ids.min() >= 0 and c.ids.max() < 1024
     assert abs(c.logits.std() - 2.0) < 0.05
-    assert synth.tiny_case("c").ref_noise is None
-    assert synth.tiny_case("b").beta == 0.0
+    assert fill_dloss(synth.tiny_case("c")).ref_noise is None
+    assert fill_dloss(synth.tiny_case("b")).beta == 0.0
 
 
 def test_token_case_structure():
-    c = synth.grpo_token_case(with_logits=False)
+    c = fill_dloss(synth.grpo_token_case(with_logits=False))
     assert c.N == 2048 and (c.adv == 0).sum() == 2
     m = c.mask.reshape(4, 512)
     lens = m.sum(axis=1)
@@ -49,11 +50,11 @@ def test_token_case_structure():
         assert m[b, :lens[b]].all() and not m[b, lens[b]:].any()
     np.testing.assert_allclose(c.dloss.sum(), 1.0, rtol=1e-6)
     assert c.ref_noise is None
-    assert synth.grpo_token_case(with_logits=False, with_ref=True).ref_noise is not None
+    assert fill_dloss(synth.grpo_token_case(with_logits=False, with_ref=True)).ref_noise is not None
 
 
 def test_sequence_case_structure():
-    c = synth.grpo_sequence_case(with_logits=False)
+    c = fill_dloss(synth.grpo_sequence_case(with_logits=False))
     assert (c.adv == 0).sum() == 2 and c.beta == 0.0 and c.level == "sequence"
     per_seq = c.old_noise.reshape(8, 1024)
     assert (per_seq == per_seq[:, :1]).all()   # one perturbation per sequence
@@ -69,7 +70,7 @@ def test_row_case_peak_rows():
 
 
 def test_fused_case_structure():
-    c = synth.fused_case(B=4, L=8, H=16, V=64)
+    c = fill_dloss(synth.fused_case(B=4, L=8, H=16, V=64))
     assert c.hidden.shape == (32, 16) and c.weight.shape == (64, 16)
     assert (c.adv == 0).sum() == 2
     lens = c.mask.reshape(4, 8).sum(axis=1)
@@ -81,7 +82,7 @@ def test_stored_tiny_logp_is_the_oracles():
     tests/golden/make_oracle_logp.py from the oracle alone) equal the
     oracle's on the generator's current inputs."""
     import oracle
-    c = synth.tiny_case("a")
+    c = fill_dloss(synth.tiny_case("a"))
     lp = synth.load_stored_logp("tiny", c.logits[synth.stored_check_rows("tiny")])
     lse = synth.load_stored_lse("tiny")
     want_lp, want_lse = oracle.selective_log_softmax(c.logits.astype(np.float64), c.ids,
