@@ -50,7 +50,12 @@
  *    ld_out == ld (in place).  No other output may alias an input.
  *  - Limits: shapes whose launches would need more than 2^31 - 1
  *    workgroups in one grid dimension return GRPO_ERR_SHAPE.
- *  - Thread safety: stateless and reentrant.  rows == 0 is a no-op.
+ *  - Thread safety: reentrant; every call may run from any host thread.
+ *    The row kernels keep no state.  The exception is fused_linear_grpo_chunk,
+ *    which keeps one side stream per device for the process (default
+ *    priority, made on its first call there, guarded by a mutex) and creates
+ *    and destroys a pair of events per call to fork to and join from it.
+ *    rows == 0 is a no-op.
  */
 #ifndef GRPO_ROWS_H
 #define GRPO_ROWS_H
