@@ -24,8 +24,9 @@
  * ---------------------------------------
  *  - Ownership: every array argument is a DEVICE pointer owned by the caller.
  *    The library never allocates, frees or copies device memory; the fused
- *    path uses only the workspace the caller passes.  Parameter structs are
- *    host pointers, read during the call only.
+ *    path uses only the workspace the caller passes, or, in
+ *    fused_linear_grpo_chunk_noalloc, a static device array of the library's
+ *    own.  Parameter structs are host pointers, read during the call only.
  *  - Layout: logits are row-major [rows, ld] with row r at logits + r*ld
  *    elements and the first V entries of each row used (ld >= V; a slice of a
  *    wider buffer is allowed).  Row r of a GRPO batch is token t of sequence
@@ -76,7 +77,8 @@ enum grpo_status {
   GRPO_ERR_ALIGN = 5,     /* pointer not aligned to its element size         */
   GRPO_ERR_WORKSPACE = 6, /* fused-linear workspace NULL or too small        */
   GRPO_ERR_LAUNCH = 7,    /* the HIP runtime refused a launch                */
-  GRPO_ERR_PARAM = 8      /* temperature <= 0, eps out of range, bad level   */
+  GRPO_ERR_PARAM = 8,     /* temperature <= 0, eps out of range, bad level   */
+  GRPO_ERR_SCRATCH = 9    /* chunk needs more than the no-alloc scratch      */
 };
 
 enum grpo_dtype { GRPO_F32 = 0, GRPO_BF16 = 1 };
@@ -275,6 +277,33 @@ int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t
 
 /* Workspace bytes fused_linear_grpo_chunk needs for R rows (0 on bad sizes). */
 size_t fused_linear_grpo_workspace_bytes(int64_t rows, int64_t V, int64_t H);
+
+/* ------------------------------------------------------------------------
+ * fused_linear_grpo_chunk_noalloc -- fused_linear_grpo_chunk for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, results
+ * and determinism as fused_linear_grpo_chunk (bit-identical outputs), minus
+ * the workspace: the chunk's workspace is a static device array of the
+ * library's own, 384 MiB (402653184 bytes), of which each device that calls
+ * this entry point holds one copy until the process ends.  Every step runs
+ * on `stream` (no side stream, no events): the call creates and allocates
+ * nothing.
+ * Limit: fused_linear_grpo_workspace_bytes(nseq*L, V, H) <= 402653184 (one
+ * 1024-token sequence at V = 151936, H = 1024 needs about 363 MiB); a larger
+ * chunk returns GRPO_ERR_SCRATCH before anything is enqueued.
+ * Concurrency: all calls on one device share its array, and nothing of it
+ * needs to start zeroed (every step writes what a later one reads), so calls
+ * ordered on one stream are safe; calls that overlap on one device (other
+ * streams, other host threads) race on the array and give wrong results.
+ * Other errors as for fused_linear_grpo_chunk; GRPO_ERR_LAUNCH also when the
+ * runtime cannot give the array's device address.
+ * ------------------------------------------------------------------------ */
+int fused_linear_grpo_chunk_noalloc(const void* hidden, int64_t nseq, int64_t L, int64_t H,
+                                    const void* weight, int64_t V, const int64_t* ids,
+                                    const float* old_logp, const float* ref_logp,
+                                    const float* adv, const uint8_t* mask, const float* dloss,
+                                    const grpo_params* p, float* loss_accum, float* grad_hidden,
+                                    float* grad_weight, void* stream);
 
 /* ------------------------------------------------------------------------
  * grpo_gemm_bf16 -- the bf16 matrix-core product the fused-linear path is

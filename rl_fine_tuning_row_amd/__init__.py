@@ -11,4 +11,5 @@ from ._lib import (  # noqa: F401
     grpo_logits_fwd, grpo_logits_fwd_bwd, header_functions, logits_partials,
     lib, selective_log_softmax, selective_log_softmax_bwd,
     entropy_from_logits_bwd, grpo_group_advantages, grpo_loss_weights, GRPO_REDUCE,
+    fused_linear_grpo_chunk_noalloc, NOALLOC_SCRATCH_BYTES,
 )

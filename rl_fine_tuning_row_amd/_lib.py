@@ -25,7 +25,8 @@ GRPO_FLAG_FORCE_DENSE = 1
 GRPO_REDUCE = {"token": 0, "sequence": 1, "constant": 2}
 STATUS = {0: "GRPO_OK", 1: "GRPO_ERR_NULL", 2: "GRPO_ERR_SHAPE", 3: "GRPO_ERR_STRIDE",
           4: "GRPO_ERR_DTYPE", 5: "GRPO_ERR_ALIGN", 6: "GRPO_ERR_WORKSPACE",
-          7: "GRPO_ERR_LAUNCH", 8: "GRPO_ERR_PARAM"}
+          7: "GRPO_ERR_LAUNCH", 8: "GRPO_ERR_PARAM", 9: "GRPO_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 384 << 20  # the static scratch of fused_linear_grpo_chunk_noalloc
 
 
 class GrpoParams(ctypes.Structure):
@@ -59,6 +60,8 @@ _SIGS = {
     "fused_linear_grpo_chunk": [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
                                 ctypes.POINTER(GrpoParams), _P, _P, _P, _P, ctypes.c_size_t, _P],
     "fused_linear_grpo_workspace_bytes": [_I64, _I64, _I64],
+    "fused_linear_grpo_chunk_noalloc": [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(GrpoParams), _P, _P, _P, _P],
     "grpo_gemm_bf16": [_P, _I, _I64, _P, _I, _I64, _P, _I64, _I64, _I64, _I64, _I, _P],
     "grpo_gemm_bf16_logits": [_P, _I64, _P, _I64, _I64, _I64, _I64, _F, _P, _P, _I64, _P, _P,
                               _P],
@@ -434,6 +437,40 @@ def fused_linear_grpo_chunk(hidden, weight, ids, old_logp, adv, mask, dloss, nse
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream))
     _check("fused_linear_grpo_chunk", st)
+    return loss_accum, grad_hidden, grad_weight
+
+
+def fused_linear_grpo_chunk_noalloc(hidden, weight, ids, old_logp, adv, mask, dloss, nseq, L, *,
+                                    ref_logp=None, temperature=1.0, beta=0.0, eps_low=0.2,
+                                    eps_high=0.2, loss_accum, grad_hidden, grad_weight,
+                                    stream=None):
+    """fused_linear_grpo_chunk on the library's static scratch: the outputs
+    must be given (nothing is allocated here either).  Returns them."""
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if not (hidden.is_cuda and weight.is_cuda and hidden.is_contiguous() and weight.is_contiguous()):
+        raise ValueError("hidden and weight must be contiguous device tensors")
+    R, H = hidden.shape
+    V, H2 = weight.shape
+    if H2 != H or R != nseq * L:
+        raise ValueError("shape mismatch: hidden [nseq*L, H], weight [V, H]")
+    f32 = torch.float32
+    for t, dt, n, nm in ((ids, torch.int64, R, "ids"), (old_logp, f32, R, "old_logp"),
+                         (ref_logp, f32, R, "ref_logp"), (adv, f32, nseq, "adv"),
+                         (mask, torch.uint8, R, "mask"), (dloss, f32, R, "dloss"),
+                         (loss_accum, f32, 1, "loss_accum"), (grad_hidden, f32, R * H, "grad_hidden"),
+                         (grad_weight, f32, V * H, "grad_weight")):
+        _need(t, dt, n, nm)
+    if loss_accum is None or grad_hidden is None or grad_weight is None:
+        raise ValueError("loss_accum, grad_hidden and grad_weight must be given")
+    p = _params(temperature, beta, eps_low, eps_high, "token")
+    st = lib().fused_linear_grpo_chunk_noalloc(_ptr(hidden), nseq, L, H, _ptr(weight), V,
+                                               _ptr(ids), _ptr(old_logp), _ptr(ref_logp),
+                                               _ptr(adv), _ptr(mask), _ptr(dloss),
+                                               ctypes.byref(p), _ptr(loss_accum),
+                                               _ptr(grad_hidden), _ptr(grad_weight),
+                                               _stream(stream))
+    _check("fused_linear_grpo_chunk_noalloc", st)
     return loss_accum, grad_hidden, grad_weight
 
 

@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "fused_internal.hpp"
 #include "gemm_mfma.hpp"
 #include "grpo_rows.h"
 #include "host_common.hpp"
@@ -269,20 +270,30 @@ extern "C" size_t fused_linear_grpo_workspace_bytes(int64_t rows, int64_t V, int
   return ws_layout(rows, V, H).total;
 }
 
-extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t H,
-                                       const void* weight, int64_t V, const int64_t* ids,
-                                       const float* old_logp, const float* ref_logp,
-                                       const float* adv, const uint8_t* mask, const float* dloss,
-                                       const grpo_params* p, float* loss_accum,
-                                       float* grad_hidden, float* grad_weight, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  int st = check_fused(hidden, nseq, L, H, weight, V, ids, old_logp, ref_logp, adv, mask, dloss,
-                       p, loss_accum, grad_hidden, grad_weight, workspace);
-  if (st != GRPO_OK || nseq == 0) return st;
+namespace grpo {
+
+int fused_chunk_check(const void* hidden, int64_t nseq, int64_t L, int64_t H, const void* weight,
+                      int64_t V, const int64_t* ids, const float* old_logp, const float* ref_logp,
+                      const float* adv, const uint8_t* mask, const float* dloss,
+                      const grpo_params* p, float* loss_accum, float* grad_hidden,
+                      float* grad_weight) {
+  // the workspace is checked by the caller (a buffer of its own, or the
+  // no-alloc entry point's static scratch); any non-null stand-in passes here
+  alignas(256) static char placeholder[1];
+  return check_fused(hidden, nseq, L, H, weight, V, ids, old_logp, ref_logp, adv, mask, dloss, p,
+                     loss_accum, grad_hidden, grad_weight, placeholder);
+}
+
+size_t fused_chunk_workspace(int64_t R, int64_t V, int64_t H) { return ws_layout(R, V, H).total; }
+
+int fused_chunk_run(const void* hidden, int64_t nseq, int64_t L, int64_t H, const void* weight,
+                    int64_t V, const int64_t* ids, const float* old_logp, const float* ref_logp,
+                    const float* adv, const float* dloss, const grpo_params* p,
+                    float* loss_accum, float* grad_hidden, float* grad_weight, void* workspace,
+                    hipStream_t s, bool use_side_stream) {
+  int st = GRPO_OK;
   const int64_t R = nseq * L;
   const WsLayout w = ws_layout(R, V, H);
-  if (workspace_bytes < w.total) return GRPO_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(workspace);
   uint16_t* z = reinterpret_cast<uint16_t*>(base + w.z_off);
   uint16_t* dz = z;  // the backward overwrites z in place
@@ -389,7 +400,7 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   // 5./6. the two gradient products, grad_weight's on the side stream
   hipStream_t s3 = s;
   hipEvent_t fork = nullptr, join = nullptr;
-  if (hipStream_t side = side_stream()) {
+  if (hipStream_t side = use_side_stream ? side_stream() : nullptr) {
     if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
         hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
         hipEventRecord(fork, s) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess) {
@@ -446,4 +457,22 @@ extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t
   if (fork != nullptr) (void)hipEventDestroy(fork);
   if (join != nullptr) (void)hipEventDestroy(join);
   return status;
+}
+
+}  // namespace grpo
+
+extern "C" int fused_linear_grpo_chunk(const void* hidden, int64_t nseq, int64_t L, int64_t H,
+                                       const void* weight, int64_t V, const int64_t* ids,
+                                       const float* old_logp, const float* ref_logp,
+                                       const float* adv, const uint8_t* mask, const float* dloss,
+                                       const grpo_params* p, float* loss_accum,
+                                       float* grad_hidden, float* grad_weight, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  int st = check_fused(hidden, nseq, L, H, weight, V, ids, old_logp, ref_logp, adv, mask, dloss,
+                       p, loss_accum, grad_hidden, grad_weight, workspace);
+  if (st != GRPO_OK || nseq == 0) return st;
+  if (workspace_bytes < ws_layout(nseq * L, V, H).total) return GRPO_ERR_WORKSPACE;
+  return fused_chunk_run(hidden, nseq, L, H, weight, V, ids, old_logp, ref_logp, adv, dloss, p,
+                         loss_accum, grad_hidden, grad_weight, workspace,
+                         static_cast<hipStream_t>(stream), true);
 }

@@ -1098,6 +1098,8 @@ extern "C" const char* grpo_status_string(int status) {
     case GRPO_ERR_WORKSPACE: return "workspace NULL or too small";
     case GRPO_ERR_LAUNCH: return "kernel launch failed";
     case GRPO_ERR_PARAM: return "invalid loss parameter";
+    case GRPO_ERR_SCRATCH:
+      return "chunk needs more workspace than the no-alloc entry point's 384 MiB scratch";
     default: return "unknown status";
   }
 }

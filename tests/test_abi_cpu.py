@@ -8,7 +8,7 @@ import pytest
 import rl_fine_tuning_row_amd as grl
 from rl_fine_tuning_row_amd._lib import GrpoParams
 
-OK, NULL, SHAPE, STRIDE, DTYPE, ALIGN, WORKSPACE, LAUNCH, PARAM = range(9)
+OK, NULL, SHAPE, STRIDE, DTYPE, ALIGN, WORKSPACE, LAUNCH, PARAM, SCRATCH = range(10)
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
 FAKE_ODD = ctypes.c_void_p(0x10002)   # aligned for bf16, not for fp32
 
@@ -27,7 +27,7 @@ def test_exports_every_header_function(L):
 
 
 def test_status_strings(L):
-    for s in range(9):
+    for s in range(10):
         assert L.grpo_status_string(s)
     assert L.grpo_status_string(99) == b"unknown status"
 
@@ -112,6 +112,28 @@ def test_fused_workspace_query(L):
     assert (L.fused_linear_grpo_workspace_bytes(1024, 151936, 1024)
             >= 1024 * 151936 * 2 + 2 * halves * 1024 * 4)
     assert L.fused_linear_grpo_workspace_bytes(-1, 100, 64) == 0
+
+
+def test_fused_noalloc_validation(L):
+    """The entry point that allocates nothing rejects bad arguments, and a
+    chunk whose workspace exceeds its 384 MiB static scratch, on the host."""
+    f = L.fused_linear_grpo_chunk_noalloc
+    p = ctypes.byref(GrpoParams(0.9, 0.04, 0.2, 0.28, 0, 0))
+    A16 = ctypes.c_void_p(0x100000)   # 16-byte aligned stand-ins, never dereferenced
+
+    def call(nseq=1, L_=16, H=64, V=256, hidden=A16, dloss=A16, params=p):
+        return f(hidden, nseq, L_, H, A16, V, A16, A16, None, A16, None, dloss, params, A16, A16,
+                 A16, None)
+    assert call(hidden=None) == NULL
+    assert call(dloss=None) == NULL
+    assert call(H=60) == SHAPE                       # H % 64
+    assert call(V=250) == SHAPE                      # V % 8
+    assert call(params=ctypes.byref(GrpoParams(0.9, 0.04, 0.2, 0.28, 1, 0))) == PARAM
+    assert call(nseq=0) == OK
+    big = L.fused_linear_grpo_workspace_bytes(2048, 151936, 1024)
+    assert big > (384 << 20)
+    assert call(nseq=2, L_=1024, H=1024, V=151936) == SCRATCH
+    assert L.fused_linear_grpo_workspace_bytes(1024, 151936, 1024) <= (384 << 20)
 
 
 def test_entropy_bwd_validation(L):
