@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4)
     ap.add_argument("--strided", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unchunked", action="store_true",
+                    help="fused-linear: skip the unchunked composition's memory comparison")
     ap.add_argument("--no-configs", action="store_true",
                     help="default workload only: skip the other workloads' measurements")
     ap.add_argument("--copy-probe", action="store_true",
@@ -754,8 +756,9 @@ def run_fused(args, torch, grl, synth):
     res["steps"] = steps
     del ws
     torch.cuda.empty_cache()
-    res["memory"] = fused_memory(torch, grl, case, h, W, ids, old_t, ref_t, adv, mask, dl, kw,
-                                 base_bytes, peak_chunked, ms)
+    if not args.no_unchunked:
+        res["memory"] = fused_memory(torch, grl, case, h, W, ids, old_t, ref_t, adv, mask, dl,
+                                     kw, base_bytes, peak_chunked, ms)
     # the dominant kernel, the logits product with its statistics epilogue,
     # timed alone on the first chunk's kept rows: back-to-back launches
     # between two events on the launch stream

@@ -145,6 +145,15 @@ struct PipeOp<ROWS, BK, true> {
                                                  int r0, int k0, int i) {
     return *reinterpret_cast<const v4u*>(P + int64_t(r0 + row_of(i)) * ld + k0 + k_of(i));
   }
+  // the same address split into a wave-uniform part (one per K step) and the
+  // lane's chunk offset (the same every step)
+  __device__ __forceinline__ static int64_t chunk_offset(int64_t ld, int i) {
+    return int64_t(row_of(i)) * ld + k_of(i);
+  }
+  __device__ __forceinline__ static const uint16_t* step_base(const uint16_t* P, int64_t ld, int r0,
+                                                              int k0) {
+    return P + int64_t(r0) * ld + k0;
+  }
   // requires extent >= 1 and kend >= 8
   __device__ __forceinline__ static v4u load_one_clamped(const uint16_t* __restrict__ P,
                                                          int64_t ld, int extent, int r0, int k0,
@@ -179,6 +188,13 @@ struct PipeOp<ROWS, BK, false> {
   __device__ __forceinline__ static v4u load_one(const uint16_t* __restrict__ P, int64_t ld,
                                                  int r0, int k0, int i) {
     return *reinterpret_cast<const v4u*>(P + int64_t(k0 + k_of(i)) * ld + r0 + col_of(i));
+  }
+  __device__ __forceinline__ static int64_t chunk_offset(int64_t ld, int i) {
+    return int64_t(k_of(i)) * ld + col_of(i);
+  }
+  __device__ __forceinline__ static const uint16_t* step_base(const uint16_t* P, int64_t ld, int r0,
+                                                              int k0) {
+    return P + int64_t(k0) * ld + r0;
   }
   // requires extent % 8 == 0, extent >= 8 and kend >= 1
   __device__ __forceinline__ static v4u load_one_clamped(const uint16_t* __restrict__ P,
@@ -352,6 +368,15 @@ __device__ __forceinline__ void pipe_mainloop(
 
   v4u r[NW];
   uint32_t in_bits = ~0u;
+  // interior tiles: each chunk's address is a wave-uniform base for the K
+  // step (scalar arithmetic) plus the lane's fixed offset, so a load costs one
+  // 64-bit add instead of a 64-bit multiply per chunk and step
+  int64_t off[NW];
+  if constexpr (!EDGE) {
+#pragma unroll
+    for (int c = 0; c < NW; ++c)
+      off[c] = c < NA ? OA::chunk_offset(g.lda, c) : OB::chunk_offset(g.ldb, c - NA);
+  }
   auto load_chunk = [&](int c, int k) {
     if constexpr (EDGE) {
       bool in;
@@ -359,8 +384,9 @@ __device__ __forceinline__ void pipe_mainloop(
       else r[c] = OB::load_one_clamped(g.B, g.ldb, g.N, n0, k, kend, c - NA, in);
       in_bits = in ? (in_bits | (1u << c)) : (in_bits & ~(1u << c));
     } else {
-      if (c < NA) r[c] = OA::load_one(g.A, g.lda, m0, k, c);
-      else r[c] = OB::load_one(g.B, g.ldb, n0, k, c - NA);
+      const uint16_t* base = c < NA ? OA::step_base(g.A, g.lda, m0, k)
+                                    : OB::step_base(g.B, g.ldb, n0, k);
+      r[c] = *reinterpret_cast<const v4u*>(base + off[c]);
     }
   };
   auto store_chunk = [&](int c, int b) {
