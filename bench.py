@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4)
     ap.add_argument("--strided", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="grpo-token: skip the with-reference reading's timing (profiling runs)")
     ap.add_argument("--no-unchunked", action="store_true",
                     help="fused-linear: skip the unchunked composition's memory comparison")
     ap.add_argument("--no-configs", action="store_true",
@@ -447,7 +449,7 @@ def run_grpo(args, torch, grl, synth, level):
                     "between steps (warm cache); not the reported value",
             "ms": round(warm_ms, 5), "GB/s": round(one_bytes / (warm_ms * 1e-3) / 1e9, 1)}
     res["skip_ab"] = skip_ab(sets, args.steps, torch)
-    if level == "token" and ref is not None:
+    if level == "token" and ref is not None and not args.no_reference:
         res["with_reference"] = with_reference(sets, args.steps, torch, N, V)
     if not args.no_cpu_baseline:
         w = oracle_token_weights(case)
