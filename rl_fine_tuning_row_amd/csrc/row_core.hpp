@@ -205,14 +205,61 @@ __device__ __forceinline__ Stat wave_reduce_stat(Stat st, float c) {
   return st;
 }
 
+// A wave's lane states merged with one rescale per lane: the wave's max M
+// first, then each lane's sums moved from its own reference fl(m c) to
+// fl(M c) (one exp2, as in stat_tile), then plain sums.  Max and sum are
+// commutative, so every lane ends with the same bits.  The result is
+// referenced to the exact M c.  (Merging pairwise at each shuffle costs two
+// exp2 per step.)
+template <bool NEED_T>
+__device__ __forceinline__ Stat wave_reduce_rescaled(Stat st, float c) {
+#pragma clang fp contract(off)
+  float M = st.m;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  const float dl = st.m * c - M * c;  // <= 0, the two rounded references
+  const float f = exp2_fast(dl);
+  Stat r;
+  r.m = M;
+  r.s = f * st.s;
+  r.t = NEED_T ? f * fmaf(dl, st.s, st.t) : 0.0f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    r.s += __shfl_xor(r.s, off, 64);
+    if (NEED_T) r.t += __shfl_xor(r.t, off, 64);
+  }
+  stat_exact<NEED_T>(r, c);
+  return r;
+}
+
+// The cross-wave step of a workgroup's merge, in one wave: lane i takes
+// wave (i mod NW)'s state from sh and an xor butterfly merges the NW states.
+// The merge is not bitwise symmetric in its operands, so lanes may differ in
+// the last bit; lane 0's result is broadcast.  Every wave that runs it on
+// the same data holds the same bits.
+template <int NW, bool NEED_T>
+__device__ __forceinline__ Stat merge_wave_states(const Stat* sh, float c) {
+  static_assert((NW & (NW - 1)) == 0, "workgroup of a power-of-two number of waves");
+  Stat r = sh[threadIdx.x & (NW - 1)];
+#pragma unroll
+  for (int off = 1; off < NW; off <<= 1) {
+    Stat o;
+    o.m = __shfl_xor(r.m, off, 64);
+    o.s = __shfl_xor(r.s, off, 64);
+    o.t = NEED_T ? __shfl_xor(r.t, off, 64) : 0.0f;
+    r = stat_merge<NEED_T>(r, o, c);
+  }
+  r.m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.m)));
+  r.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.s)));
+  if (NEED_T) r.t = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.t)));
+  return r;
+}
+
 // merge the per-lane states of the workgroup; the result is valid in every
-// lane.  Fixed merge order, so the result is deterministic.
-// Across waves: lane i of every wave takes wave (i mod NW)'s state and an
-// xor butterfly merges the NW states; the merge is not bitwise symmetric in
-// its operands, so lanes may differ in the last bit and lane 0's result is
-// broadcast.  Every wave runs the same butterfly on the same data, so lane 0
-// holds the same bits in every wave.  (Merging all NW states in every lane
-// in turn keeps 3·NW floats and their temporaries live beside a
+// lane.  Fixed merge order, so the result is deterministic: each wave merges
+// its lanes, then every wave runs the cross-wave butterfly above on the
+// waves' states (the same bits in every wave).  (Merging all NW states in
+// every lane in turn keeps 3·NW floats and their temporaries live beside a
 // register-resident row.)
 // `st` is a lane's streamed state (sums referenced to fl(m c)).
 template <int WG, bool NEED_T>
@@ -223,24 +270,11 @@ __device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
     return st;
   } else {
     constexpr int NW = WG / 64;
-    static_assert((NW & (NW - 1)) == 0, "workgroup of a power-of-two number of waves");
     __shared__ Stat sh[NW];
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) sh[w] = st;
     __syncthreads();
-    Stat r = sh[threadIdx.x & (NW - 1)];
-#pragma unroll
-    for (int off = 1; off < NW; off <<= 1) {
-      Stat o;
-      o.m = __shfl_xor(r.m, off, 64);
-      o.s = __shfl_xor(r.s, off, 64);
-      o.t = NEED_T ? __shfl_xor(r.t, off, 64) : 0.0f;
-      r = stat_merge<NEED_T>(r, o, c);
-    }
-    r.m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.m)));
-    r.s = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.s)));
-    if (NEED_T) r.t = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(r.t)));
-    return r;
+    return merge_wave_states<NW, NEED_T>(sh, c);
   }
 }
 

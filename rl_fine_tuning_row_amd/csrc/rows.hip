@@ -446,34 +446,51 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   // way, so its sums are garbage (possibly inf, and inf * 0 = NaN in the
   // merge).  It contributes the empty state instead.
   if (!(tid < nvec || has_tail)) stat_init(st);
-  st = block_reduce_stat<WG, NEED_T>(st, c);
-
-  // per-token epilogue, computed alike in every lane
-  const float logS = logf(st.s);
-  const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
-  const float zy = valid ? sh_zy : __builtin_nanf("");
-  const float lse = st.m / f.T + logS;
-  const float logp = (zy - st.m) / f.T - logS;
-  float kl = 0.0f;
-  if (f.ref_logp != nullptr) {
-    const float d = ref_lp - logp;
-    kl = expm1f(d) - d;
+  // Each wave merges its lanes; then wave 0 alone merges the waves' states
+  // and runs the per-token epilogue, and hands the row's dlogp and lse to
+  // the other waves through LDS.  (Every wave computing them alike cost a
+  // sixth of the kernel's VALU instructions, the transcendental-heavy
+  // epilogue fifteen times over.)
+  constexpr int NW = WG / 64;
+  st = wave_reduce_rescaled<NEED_T>(st, c);
+  __shared__ Stat sh_st[NW];
+  __shared__ float sh_g, sh_lse;
+  if ((tid & 63) == 0) sh_st[tid >> 6] = st;
+  __syncthreads();
+  if (tid < 64) {
+    st = merge_wave_states<NW, NEED_T>(sh_st, c);
+    // per-token epilogue, computed alike in the lanes of wave 0
+    const float logS = logf(st.s);
+    const float H = NEED_T ? logS - kLn2 * st.t / st.s : 0.0f;
+    const float zy = valid ? sh_zy : __builtin_nanf("");
+    const float lse = st.m / f.T + logS;
+    const float logp = (zy - st.m) / f.T - logS;
+    float kl = 0.0f;
+    if (f.ref_logp != nullptr) {
+      const float d = ref_lp - logp;
+      kl = expm1f(d) - d;
+    }
+    const Ppo q = ppo_terms(logp - old_lp, A, f.lo, f.hi);
+    float klg = 0.0f;
+    if (f.ref_logp != nullptr && f.beta != 0.0f) klg = -f.beta * expm1f(ref_lp - logp);
+    const float g = uniform(((q.clipped ? 0.0f : -q.ratio * A) + klg) * w);
+    if (tid == 0) {
+      if (!valid && f.err_count != nullptr) atomicAdd(f.err_count, 1);
+      f.logp[r] = logp;
+      f.lse[r] = lse;
+      if (f.entropy != nullptr) f.entropy[r] = H;
+      if (f.kl != nullptr) f.kl[r] = kl;
+      f.loss[r] = q.pg + (f.beta != 0.0f ? f.beta * kl : 0.0f);
+      if (f.is_clipped != nullptr) f.is_clipped[r] = q.clipped ? 1 : 0;
+      if (a.zero_row != nullptr) a.zero_row[r] = g == 0.0f ? 1 : 0;
+      sh_g = g;
+      sh_lse = lse;
+    }
   }
-  const Ppo q = ppo_terms(logp - old_lp, A, f.lo, f.hi);
-  float klg = 0.0f;
-  if (f.ref_logp != nullptr && f.beta != 0.0f) klg = -f.beta * expm1f(ref_lp - logp);
-  const float g = uniform(((q.clipped ? 0.0f : -q.ratio * A) + klg) * w);
+  __syncthreads();
+  const float g = uniform(sh_g);
+  const float lse = uniform(sh_lse);
   const bool zero = (g == 0.0f);
-  if (tid == 0) {
-    if (!valid && f.err_count != nullptr) atomicAdd(f.err_count, 1);
-    f.logp[r] = logp;
-    f.lse[r] = lse;
-    if (f.entropy != nullptr) f.entropy[r] = H;
-    if (f.kl != nullptr) f.kl[r] = kl;
-    f.loss[r] = q.pg + (f.beta != 0.0f ? f.beta * kl : 0.0f);
-    if (f.is_clipped != nullptr) f.is_clipped[r] = q.clipped ? 1 : 0;
-    if (a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
-  }
 
   TIn* __restrict__ out = static_cast<TIn*>(a.dlogits) + r * a.ld_out;
   u32x4* __restrict__ ov = reinterpret_cast<u32x4*>(out);
