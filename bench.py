@@ -136,11 +136,24 @@ def stored_traffic(kernel: str, workload: str):
     return e["fetch_bytes"] + e["write_bytes"]
 
 
+# GPU-side spin (torch's own sleep kernel) queued after the synchronize that
+# opens a timed region and before its start event: while the GPU spins, the
+# host enqueues the first launches of the region, so the region measures the
+# steps back to back rather than the host's latency in issuing the first one.
+GATE_CYCLES = 200_000
+
+
+def gate(torch):
+    torch.cuda._sleep(GATE_CYCLES)
+
+
 def timed(step_fns, steps, torch):
-    """Wall time (ms) per step of `steps` steps rotating over step_fns."""
+    """Wall time (ms) per step of `steps` steps rotating over step_fns,
+    between two events on the launch stream (opened behind the gate)."""
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gate(torch)
     t0.record()
     for i in range(steps):
         step_fns[i % len(step_fns)]()
@@ -159,6 +172,7 @@ def kernel_times(launch_lists, steps, torch):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        gate(torch)
         e0.record()
         for i in range(steps):
             launch_lists[i % len(launch_lists)][k]()
