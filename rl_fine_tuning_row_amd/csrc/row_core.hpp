@@ -192,19 +192,6 @@ __device__ __forceinline__ Stat stat_merge(const Stat& a, const Stat& b, float c
   return r;
 }
 
-template <bool NEED_T>
-__device__ __forceinline__ Stat wave_reduce_stat(Stat st, float c) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    Stat o;
-    o.m = __shfl_xor(st.m, off, 64);
-    o.s = __shfl_xor(st.s, off, 64);
-    o.t = NEED_T ? __shfl_xor(st.t, off, 64) : 0.0f;
-    st = stat_merge<NEED_T>(st, o, c);
-  }
-  return st;
-}
-
 // A wave's lane states merged with one rescale per lane: the wave's max M
 // first, then each lane's sums moved from its own reference fl(m c) to
 // fl(M c) (one exp2, as in stat_tile), then plain sums.  Max and sum are
@@ -255,17 +242,14 @@ __device__ __forceinline__ Stat merge_wave_states(const Stat* sh, float c) {
   return r;
 }
 
-// merge the per-lane states of the workgroup; the result is valid in every
-// lane.  Fixed merge order, so the result is deterministic: each wave merges
-// its lanes, then every wave runs the cross-wave butterfly above on the
-// waves' states (the same bits in every wave).  (Merging all NW states in
-// every lane in turn keeps 3·NW floats and their temporaries live beside a
-// register-resident row.)
+// merge the per-lane states of the workgroup for lane 0: each wave merges
+// its lanes (one rescale per lane), then wave 0 alone merges the waves'
+// states; the result is lane 0's and deterministic (fixed merge order).
+// Other lanes get an unspecified state (callers use lane 0's only).
 // `st` is a lane's streamed state (sums referenced to fl(m c)).
 template <int WG, bool NEED_T>
 __device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
-  stat_exact<NEED_T>(st, c);
-  st = wave_reduce_stat<NEED_T>(st, c);
+  st = wave_reduce_rescaled<NEED_T>(st, c);
   if constexpr (WG == 64) {
     return st;
   } else {
@@ -274,6 +258,7 @@ __device__ __forceinline__ Stat block_reduce_stat(Stat st, float c) {
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) sh[w] = st;
     __syncthreads();
+    if (w != 0) return st;
     return merge_wave_states<NW, NEED_T>(sh, c);
   }
 }
