@@ -25,6 +25,12 @@ namespace grpo {
 // ---------------------------------------------------------------------------
 // forward: one pass over the row
 // ---------------------------------------------------------------------------
+// Values past the row end in a lane's registers: large, negative and finite,
+// they add nothing to a max or a sum taken against a real element.
+template <typename TIn> struct Fill;
+template <> struct Fill<uint16_t> { static constexpr uint32_t bits = 0xF149F149u; };  // bf16 ~ -1e30
+template <> struct Fill<float> { static constexpr uint32_t bits = 0xF149F2CAu; };     // -1e30f
+
 template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
 __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, float c) {
   Stat st;
@@ -44,10 +50,16 @@ __device__ __forceinline__ Stat scan_row(const TIn* __restrict__ row, int V, flo
       for (int u = 0; u < UNROLL; ++u) Vec<TIn>::unpack(v[u], x + u * VE);
       stat_tile<UNROLL * VE, NEED_T>(st, x, c);
     }
-    for (; i < nvec; i += WG) {
-      float x[VE];
-      Vec<TIn>::unpack(load16<NTL>(rv + i), x);
-      stat_tile<VE, NEED_T>(st, x, c);
+    if (i < nvec) {  // the last, partial batch: its loads issued at once
+      const u32x4 fill = {Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits};
+      u32x4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        v[u] = i + u * WG < nvec ? load16<NTL>(rv + i + u * WG) : fill;
+      float x[UNROLL * VE];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) Vec<TIn>::unpack(v[u], x + u * VE);
+      stat_tile<UNROLL * VE, NEED_T>(st, x, c);
     }
     const int j = nvec * VE + tid;
     if (j < V) {
@@ -356,9 +368,6 @@ struct FusedArgs {
 // compiler keeping every unpacked float alive across the passes.
 __device__ __forceinline__ void keep_packed(u32x4& v) { asm volatile("" : "+v"(v)); }
 
-template <typename TIn> struct Fill;
-template <> struct Fill<uint16_t> { static constexpr uint32_t bits = 0xF149F149u; };  // bf16 ~ -1e30
-template <> struct Fill<float> { static constexpr uint32_t bits = 0xF149F2CAu; };     // -1e30f
 
 template <typename TIn, int WG, int VPT, bool NEED_T>
 __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
