@@ -584,14 +584,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
       // no column left keeps the empty state rather than fold the fill.
       const int nv = g.N - nw;  // columns of this wave's half inside C
       float x[4 * 16];          // x[16 jj + r] = acc[i][jj][r]
-#pragma unroll
-      for (int jj = 0; jj < TN; ++jj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          x[16 * jj + r] = 32 * jj + 8 * (r >> 2) < nv ? acc[i][jj][r] : kNegBig;
       Stat st;
       stat_init(st);
-      if (nv > 0) stat_tile<64, false>(st, x, c);
+      if (nv >= BN / 2) {  // the whole half inside C: no per-element select
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[16 * jj + r] = acc[i][jj][r];
+        stat_tile<64, false>(st, x, c);
+      } else if (nv > 0) {
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            x[16 * jj + r] = 32 * jj + 8 * (r >> 2) < nv ? acc[i][jj][r] : kNegBig;
+        stat_tile<64, false>(st, x, c);
+      }
       stat_exact<false>(st, c);
       Stat o;
       o.m = __shfl_xor(st.m, 32, 64);
