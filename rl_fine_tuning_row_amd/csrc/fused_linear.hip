@@ -101,7 +101,12 @@ WsLayout ws_layout(int64_t R, int64_t V, int64_t H) {
     o += align256(bytes);
     return at;
   };
-  w.z_off = take(size_t(R) * size_t(V) * 2);  // bf16 z, then dz in place
+  // z and h_c hold the kept rows rounded up to 64: grad_weight's product runs
+  // over that many rows, the ones past the kept count zeroed, so that its K
+  // steps are all whole (a partial last K step takes the masked path in
+  // every tile: 8-10% slower)
+  const int64_t Rp = (R + 63) / 64 * 64;
+  w.z_off = take(size_t(Rp) * size_t(V) * 2);  // bf16 z, then dz in place
   w.part_off = take(std::max(stats, splitk));  // row statistics, then split-K partial sums
   w.zy_off = take(size_t(R) * 4);
   w.logp_off = take(size_t(R) * 4);
@@ -109,8 +114,8 @@ WsLayout ws_layout(int64_t R, int64_t V, int64_t H) {
   w.loss_off = take(size_t(R) * 4);
   w.map_off = take(size_t(R) * 4);
   w.pos_off = take(size_t(R) * 4);
-  w.cnt_off = take(4);
-  w.hc_off = take(size_t(R) * size_t(H) * 2);
+  w.cnt_off = take(8);  // kept rows, then that count rounded up to 64
+  w.hc_off = take(size_t(Rp) * size_t(H) * 2);
   w.ids_off = take(size_t(R) * 8);
   w.old_off = take(size_t(R) * 4);
   w.ref_off = take(size_t(R) * 4);
@@ -164,7 +169,26 @@ __global__ __launch_bounds__(1024) void compact_rows_kernel(
     }
     __syncthreads();
   }
-  if (t == 0) *count = base_sh;
+  if (t == 0) {
+    count[0] = base_sh;
+    count[1] = (base_sh + 63) / 64 * 64;
+  }
+}
+
+// Zero rows [count[0], count[1]) of z (ldz columns, the first V written) and
+// of h_c (H columns): the rows grad_weight's product adds past the kept
+// ones.  One workgroup per row, at most 63 rows; V and H multiples of 8.
+__global__ __launch_bounds__(1024) void zero_pad_rows_kernel(const int32_t* __restrict__ count,
+                                                             uint16_t* __restrict__ z,
+                                                             int64_t ldz, int V,
+                                                             uint16_t* __restrict__ h_c, int H) {
+  const int64_t i = int64_t(count[0]) + blockIdx.x;
+  if (i >= count[1]) return;
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  uint4* zr = reinterpret_cast<uint4*>(z + i * ldz);
+  for (int v = threadIdx.x; v < V / 8; v += 1024) zr[v] = zero;
+  uint4* hr = reinterpret_cast<uint4*>(h_c + i * H);
+  for (int v = threadIdx.x; v < H / 8; v += 1024) hr[v] = zero;
 }
 
 // h_c[i] = h[map[i]] for the kept rows; one workgroup per compact row,
@@ -319,6 +343,8 @@ int fused_chunk_run(const void* hidden, int64_t nseq, int64_t L, int64_t H, cons
                      old_logp, ref_logp, adv, map, pos, cnt, ids_c, old_c, ref_c, adv_c, w_c);
   hipLaunchKernelGGL(gather_rows_kernel, dim3(unsigned(R)), dim3(256), 0, s, h, int(H), map, cnt,
                      h_c);
+  hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(63), dim3(1024), 0, s, cnt, z, int64_t(V), int(V),
+                     h_c, int(H));
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
 
   // 1. logits of the kept rows: bf16 z, row statistics and target logits
@@ -421,9 +447,9 @@ int fused_chunk_run(const void* hidden, int64_t nseq, int64_t L, int64_t H, cons
   g3.ldc = H;
   g3.M = int32_t(V);
   g3.N = int32_t(H);
-  g3.K = int32_t(R);
-  g3.k_per_split = int32_t(((R + 63) / 64) * 64);
-  g3.dev_k = cnt;
+  g3.K = int32_t((R + 63) / 64 * 64);
+  g3.k_per_split = g3.K;
+  g3.dev_k = cnt + 1;  // the kept rows rounded up to 64 (the extra rows are zero)
   if (gemm_bf16(false, false, GEMM_ACCUM, g3, 1, s3) != hipSuccess) status = GRPO_ERR_LAUNCH;
 
   // 5. grad_hidden = dz W, split over V into partial sums (the statistics' region),
