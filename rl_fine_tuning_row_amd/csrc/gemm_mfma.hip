@@ -150,6 +150,13 @@ struct PipeOp<ROWS, BK, true> {
   __device__ __forceinline__ static int64_t chunk_offset(int64_t ld, int i) {
     return int64_t(row_of(i)) * ld + k_of(i);
   }
+  // the same with the row clamped to the operand's last (extent > r0): a
+  // tile that overhangs M or N reads valid rows there, whose results are
+  // never stored
+  __device__ __forceinline__ static int64_t chunk_offset_clamped(int64_t ld, int i, int r0,
+                                                                 int extent) {
+    return int64_t(min(row_of(i), extent - 1 - r0)) * ld + k_of(i);
+  }
   __device__ __forceinline__ static const uint16_t* step_base(const uint16_t* P, int64_t ld, int r0,
                                                               int k0) {
     return P + int64_t(r0) * ld + k0;
@@ -191,6 +198,12 @@ struct PipeOp<ROWS, BK, false> {
   }
   __device__ __forceinline__ static int64_t chunk_offset(int64_t ld, int i) {
     return int64_t(k_of(i)) * ld + col_of(i);
+  }
+  // columns clamped to the last 16-byte chunk of the extent (extent % 8 == 0,
+  // extent > r0)
+  __device__ __forceinline__ static int64_t chunk_offset_clamped(int64_t ld, int i, int r0,
+                                                                 int extent) {
+    return int64_t(k_of(i)) * ld + min(col_of(i), extent - 8 - r0);
   }
   __device__ __forceinline__ static const uint16_t* step_base(const uint16_t* P, int64_t ld, int r0,
                                                               int k0) {
@@ -375,7 +388,8 @@ __device__ __forceinline__ void pipe_mainloop(
   if constexpr (!EDGE) {
 #pragma unroll
     for (int c = 0; c < NW; ++c)
-      off[c] = c < NA ? OA::chunk_offset(g.lda, c) : OB::chunk_offset(g.ldb, c - NA);
+      off[c] = c < NA ? OA::chunk_offset_clamped(g.lda, c, m0, g.M)
+                      : OB::chunk_offset_clamped(g.ldb, c - NA, n0, g.N);
   }
   auto load_chunk = [&](int c, int k) {
     if constexpr (EDGE) {
@@ -516,8 +530,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
       for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
 
   if (kend > kbeg) {
-    const bool interior = (m0 + BM <= g.M) && (n0 + BN <= g.N) && ((kend - kbeg) % BK == 0);
-    if (interior) pipe_mainloop<C, A_KC, B_KC, false>(g, m0, n0, kbeg, kend, As, Bs, acc);
+    // whole K steps take the unmasked loop, also in tiles that overhang M or
+    // N (their loads clamped into the operands; the epilogues store no row or
+    // column past C); a partial K step needs the masked one
+    const bool whole_k = (kend - kbeg) % BK == 0;
+    if (whole_k) pipe_mainloop<C, A_KC, B_KC, false>(g, m0, n0, kbeg, kend, As, Bs, acc);
     else pipe_mainloop<C, A_KC, B_KC, true>(g, m0, n0, kbeg, kend, As, Bs, acc);
   }
 
