@@ -142,10 +142,13 @@ __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
 }
 
 // Forward of the chunked loss's rows from the logits product's partial
-// statistics (max and sum; no entropy): lane = row (64 rows per
-// workgroup), the NW waves each merge a strided share of the row's P
-// partials, the shares are merged in wave order (deterministic), and the
-// target logit comes from zy (fp32).
+// statistics (max and sum; no entropy): 16 rows per workgroup, four lanes of
+// every wave per row, each lane merging a strided share of the row's P
+// partials; the four lanes' states are merged by a fixed butterfly, the
+// waves' in wave order (deterministic), and the target logit comes from zy
+// (fp32).  (Sixty-four rows per workgroup left most CUs idle at a chunk's
+// few thousand rows.)
+constexpr int kPartialRows = 16;
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
                                                                     const float* __restrict__ stat,
@@ -153,7 +156,8 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
                                                                     const float* __restrict__ zy,
                                                                     int64_t rows) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t r = int64_t(blockIdx.x) * 64 + lane;
+  const int rl = lane >> 2, sub = lane & 3;
+  const int64_t r = int64_t(blockIdx.x) * kPartialRows + rl;
   const int64_t R = a.dev_rows != nullptr ? min(rows, int64_t(*a.dev_rows)) : rows;
   Stat st;
   stat_init(st);
@@ -161,17 +165,25 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
     const float* pm = stat + r;
     const float* ps = pm + int64_t(P) * sl;
 #pragma unroll 4
-    for (int p = w; p < P; p += NW) {
+    for (int p = 4 * w + sub; p < P; p += 4 * NW) {
       const Stat q = {pm[int64_t(p) * sl], ps[int64_t(p) * sl], 0.0f};
       st = stat_merge<false>(st, q, a.c);
     }
   }
-  __shared__ Stat sh[NW][64];
-  sh[w][lane] = st;
-  __syncthreads();
-  if (w != 0 || r >= R) return;
 #pragma unroll
-  for (int k = 1; k < NW; ++k) st = stat_merge<false>(st, sh[k][lane], a.c);
+  for (int off = 1; off < 4; off <<= 1) {
+    Stat o;
+    o.m = __shfl_xor(st.m, off, 64);
+    o.s = __shfl_xor(st.s, off, 64);
+    o.t = 0.0f;
+    st = stat_merge<false>(st, o, a.c);
+  }
+  __shared__ Stat sh[NW][kPartialRows];
+  if (sub == 0) sh[w][rl] = st;
+  __syncthreads();
+  if (w != 0 || sub != 0 || r >= R) return;
+#pragma unroll
+  for (int k = 1; k < NW; ++k) st = stat_merge<false>(st, sh[k][rl], a.c);
   const int64_t y = a.ids[r];
   const bool valid = y >= 0 && y < a.V;
   fwd_token_epilogue<false>(a, r, st, valid ? zy[r] : 0.0f, valid);
@@ -674,8 +686,9 @@ int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat
                         const float* zy, int64_t rows, hipStream_t s) {
   if (rows <= 0) return GRPO_OK;
   constexpr int NW = 16;
-  hipLaunchKernelGGL((row_fwd_partials_kernel<NW>), dim3(unsigned((rows + 63) / 64)),
-                     dim3(64 * NW), 0, s, a, stat, P, stat_ld, zy, rows);
+  hipLaunchKernelGGL((row_fwd_partials_kernel<NW>),
+                     dim3(unsigned((rows + kPartialRows - 1) / kPartialRows)), dim3(64 * NW), 0, s,
+                     a, stat, P, stat_ld, zy, rows);
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
