@@ -49,13 +49,16 @@ def _t(bits):
 
 @pytest.mark.parametrize("a_layout,b_layout", [(0, 0), (0, 1), (1, 1), (1, 0)])
 @pytest.mark.parametrize("M,N,K", [(128, 128, 32), (200, 264, 96), (520, 392, 1064), (8, 16, 8),
-                                   (4000, 7880, 136), (2056, 14344, 72), (4096, 8192, 200)])
+                                   (4000, 7880, 136), (2056, 14344, 72), (4096, 8192, 200),
+                                   (2056, 14344, 128), (4104, 8200, 192)])
 def test_gemm_layouts(a_layout, b_layout, M, N, K):
     """The first four shapes take the 128 x 128 block tile; (4000, 7880, 136)
     has fewer than 512 tiles of 256 x 256 but at least 512 of 256 x 128, so a
     transposed operand takes the 256 x 128 tile (K-contiguous ones the
-    128 x 128); the last two (>= 512 tiles of 256 x 256, ragged in M, N and K)
-    take the pipelined 256 x 256 x 64 tile in every layout."""
+    128 x 128); the last four (>= 512 tiles of 256 x 256) take the pipelined
+    256 x 256 x 64 tile in every layout: ragged in M, N and K (the masked
+    loop), and ragged in M and N only with whole K steps (the unmasked loop,
+    its loads clamped into the operands at the overhanging tiles)."""
     lib = require_gpu()
     say(f"gemm layouts a={a_layout} b={b_layout} M={M} N={N} K={K}")
     rng = np.random.default_rng(M * 7 + N * 3 + K)
@@ -79,7 +82,8 @@ def test_gemm_layouts(a_layout, b_layout, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,T", [(520, 1032, 136, 0.9), (300, 264, 64, 0.9), (40, 8, 8, 0.9),
-                                     (4096, 8200, 136, 0.9), (520, 1032, 136, 0.05)])
+                                     (4096, 8200, 136, 0.9), (520, 1032, 136, 0.05),
+                                     (2056, 14344, 128, 0.9)])
 def test_gemm_logits_mode(M, N, K, T):
     """The fused chunk's logits product alone (grpo_gemm_bf16_logits): against
     float64 products of the same bf16 values, z16 within the accumulation
@@ -87,11 +91,13 @@ def test_gemm_logits_mode(M, N, K, T):
     log-sum-exp of z/T within 1e-5 relative plus the bound's effect, and the
     target logit within the bound (rows with an out-of-range id untouched).
     Where the fp32 store mode runs the same pipelined tile (>= 512 tiles:
-    the last shape) the results are exact against it: z16 is the correctly
-    rounded fp32 C, zy and each max are entries of C.  N = 1032 and 264 leave
-    8 and 0 columns in the last 128-column half-tile, (40, 8, 8) is a single
-    tile.  At T = 0.05 each partial's sum must be referenced to its exact max
-    for the merged log-sum-exp to meet its bar."""
+    (4096, 8200, 136) and (2056, 14344, 128)) the results are exact against
+    it: z16 is the correctly rounded fp32 C, zy and each max are entries of
+    C.  N = 1032 and 264 leave 8 and 0 columns in the last 128-column
+    half-tile, (40, 8, 8) is a single tile, and (2056, 14344, 128) overhangs
+    M and N with whole K steps (the unmasked loop at the edge tiles).  At
+    T = 0.05 each partial's sum must be referenced to its exact max for the
+    merged log-sum-exp to meet its bar."""
     lib = require_gpu()
     say(f"gemm logits mode M={M} N={N} K={K} T={T}")
     rng = np.random.default_rng(M + N + K)
