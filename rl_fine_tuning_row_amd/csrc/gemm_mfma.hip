@@ -502,9 +502,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   if (g.dev_k != nullptr) g.K = min(g.K, *g.dev_k);
   // Workgroups are dispatched round-robin over the 8 XCDs in linear order.
   // Number the active tiles of every K-split 0 .. total-1, give each XCD an
-  // equal contiguous run of them (successive m for one n and split: tiles
-  // that share a B panel share that XCD's L2) and let the rest return, so
-  // that inactive tiles (rows past the device extent) leave no XCD idle.
+  // equal contiguous run of them and let the rest return, so that inactive
+  // tiles (rows past the device extent) leave no XCD idle.  Within a split
+  // the run takes successive m for one n (tiles that share a B panel share
+  // that XCD's L2) unless C has at most 8 column tiles: then successive n
+  // for one m, so that the 32 tiles an XCD runs at once read 8 A panels and
+  // every B panel (12 distinct panels) instead of 32 A panels and one B.
   const int tiles_m = (g.M + BM - 1) / BM;
   const int per_split = tiles_m * g.tiles_n;
   const int total = per_split * int(gridDim.y);
@@ -514,7 +517,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_pipe_kernel(GemmArgs g)
   const int xcd = id % 8, j = id / 8;
   const int t = xcd * q + min(xcd, rr) + j;
   const int z = t / per_split, tt = t % per_split;
-  const int tm = tt % tiles_m, tn = tt / tiles_m;
+  const bool n_fast = g.tiles_n <= 8;
+  const int tm = n_fast ? tt / g.tiles_n : tt % tiles_m;
+  const int tn = n_fast ? tt % g.tiles_n : tt / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = z * g.k_per_split;
   const int kend = min(g.K, kbeg + g.k_per_split);
