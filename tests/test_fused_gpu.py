@@ -50,15 +50,19 @@ def _t(bits):
 @pytest.mark.parametrize("a_layout,b_layout", [(0, 0), (0, 1), (1, 1), (1, 0)])
 @pytest.mark.parametrize("M,N,K", [(128, 128, 32), (200, 264, 96), (520, 392, 1064), (8, 16, 8),
                                    (4000, 7880, 136), (2056, 14344, 72), (4096, 8192, 200),
-                                   (2056, 14344, 128), (4104, 8200, 192)])
+                                   (2056, 14344, 128), (4104, 8200, 192),
+                                   (32776, 1032, 64), (32776, 1032, 72)])
 def test_gemm_layouts(a_layout, b_layout, M, N, K):
     """The first four shapes take the 128 x 128 block tile; (4000, 7880, 136)
     has fewer than 512 tiles of 256 x 256 but at least 512 of 256 x 128, so a
     transposed operand takes the 256 x 128 tile (K-contiguous ones the
-    128 x 128); the last four (>= 512 tiles of 256 x 256) take the pipelined
+    128 x 128); the last six (>= 512 tiles of 256 x 256) take the pipelined
     256 x 256 x 64 tile in every layout: ragged in M, N and K (the masked
     loop), and ragged in M and N only with whole K steps (the unmasked loop,
-    its loads clamped into the operands at the overhanging tiles)."""
+    its loads clamped into the operands at the overhanging tiles).  The two
+    with N = 1032 have 5 column tiles, so each XCD's run of tiles takes
+    successive n for one m (the order of the fused path's gradient
+    products)."""
     lib = require_gpu()
     say(f"gemm layouts a={a_layout} b={b_layout} M={M} N={N} K={K}")
     rng = np.random.default_rng(M * 7 + N * 3 + K)
