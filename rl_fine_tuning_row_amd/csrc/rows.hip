@@ -2,12 +2,13 @@
 // grpo_logits_fwd, grpo_logits_bwd, entropy_from_logits,
 // selective_log_softmax, selective_log_softmax_bwd.
 //
-// One workgroup per row.  Lanes stream the row with 128-bit loads (8 bf16 or
-// 4 fp32 per lane), UNROLL vectors in flight per lane, fold each register
-// tile into the online softmax state (row_core.hpp), reduce across the wave
-// with lane shuffles and across waves through LDS, and lane 0 writes the
-// per-row scalars.  The backward computes the row's dlogp first; it is the
-// same in every lane (readfirstlane), so the all-zero early path
+// One workgroup per row (the backward splits rows past 64 KB into 64 KB
+// chunks, one workgroup each).  Lanes stream the row with 128-bit loads (8
+// bf16 or 4 fp32 per lane), UNROLL vectors in flight per lane, fold each
+// register tile into the online softmax state (row_core.hpp), reduce across
+// the wave with lane shuffles and across waves through LDS, and lane 0 writes
+// the per-row scalars.  The backward computes the row's dlogp first; it is
+// the same in every lane (readfirstlane), so the all-zero early path
 // [Liger-Kernel PR #1550 analysis, "Code analysis": the added
 // ``if dlogp == 0.0`` early return] is a scalar branch that writes zeros
 // without touching the logits.
@@ -258,17 +259,19 @@ __device__ __forceinline__ void store_vec(TOut* __restrict__ out, int i, const f
   }
 }
 
+// vectors [beg, end) of the row, and the elements past its last whole vector
+// when `tail`; without VEC the whole row
 template <typename TIn, typename TOut, int WG, bool VEC>
-__device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float value) {
+__device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float value, int beg,
+                                         int end, bool tail) {
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
     float x[VE];
 #pragma unroll
     for (int k = 0; k < VE; ++k) x[k] = value;
-    const int nvec = V / VE;
-    for (int i = threadIdx.x; i < nvec; i += WG) store_vec<TIn, TOut>(out, i, x);
-    const int j = nvec * VE + threadIdx.x;
-    if (j < V) store_elem(out + j, value);
+    for (int i = beg + int(threadIdx.x); i < end; i += WG) store_vec<TIn, TOut>(out, i, x);
+    const int j = (V / VE) * VE + threadIdx.x;
+    if (tail && j < V) store_elem(out + j, value);
   } else {
     for (int j = threadIdx.x; j < V; j += WG) store_elem(out + j, value);
   }
@@ -277,20 +280,30 @@ __device__ __forceinline__ void fill_row(TOut* __restrict__ out, int V, float va
 // ENT: the entropy backward, dz_j = -(g/T) p_j (log p_j + H), no sampled id
 template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC, bool NTL, bool ENT = false>
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
-  const int64_t r = blockIdx.x;
+  // a.nchunk workgroups per row, each on WG * UNROLL consecutive vectors (the
+  // last one on the rest of the row and its tail elements)
+  const int64_t r = int64_t(blockIdx.x) / a.nchunk;
+  const int ch = int(int64_t(blockIdx.x) - r * a.nchunk);
+  const bool last = ch == a.nchunk - 1;
   if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const float g = uniform(row_dlogp<TIn, WG>(a, r));
   const int64_t y = ENT ? 0 : a.ids[r];
   const bool valid = ENT || (y >= 0 && y < a.V);
   TOut* __restrict__ out = static_cast<TOut*>(a.dlogits) + r * a.ld_out;
   const bool zero = (g == 0.0f);
-  if (threadIdx.x == 0 && a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
-  if (!valid) {
-    fill_row<TIn, TOut, WG, false>(out, a.V, __builtin_nanf(""));
+  if (threadIdx.x == 0 && ch == 0 && a.zero_row != nullptr) a.zero_row[r] = zero ? 1 : 0;
+  constexpr int VEN = VEC ? Vec<TIn>::N : 1;
+  const int nvec_all = a.V / VEN;
+  const int vbeg = ch * (WG * UNROLL);
+  const int vend = last ? nvec_all : vbeg + WG * UNROLL;
+  if (!valid) {  // this workgroup's elements, one at a time
+    const int e1 = last ? a.V : vend * VEN;
+    for (int j = vbeg * VEN + int(threadIdx.x); j < e1; j += WG)
+      store_elem(out + j, __builtin_nanf(""));
     return;
   }
   if (zero && !a.force_dense) {  // early path: no logits read, no exp
-    fill_row<TIn, TOut, WG, VEC>(out, a.V, 0.0f);
+    fill_row<TIn, TOut, WG, VEC>(out, a.V, 0.0f, vbeg, vend, last);
     return;
   }
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
@@ -308,9 +321,9 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   if constexpr (VEC) {
     constexpr int VE = Vec<TIn>::N;
     const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-    const int nvec = a.V / VE;
+    const int nvec = vend;
     const int vy = yi / VE, ky = yi % VE;
-    int i = threadIdx.x;
+    int i = vbeg + int(threadIdx.x);
     for (; i + (UNROLL - 1) * WG < nvec; i += UNROLL * WG) {
       u32x4 v[UNROLL];
 #pragma unroll
@@ -341,8 +354,8 @@ __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
       }
       store_vec<TIn, TOut>(out, i, x);
     }
-    const int j = nvec * VE + threadIdx.x;
-    if (j < a.V) {
+    const int j = nvec_all * VE + threadIdx.x;
+    if (last && j < a.V) {
       float d = grad_elem(load_elem(row + j));
       if (!ENT && j == yi) d += coef;
       store_elem(out + j, d);
@@ -581,9 +594,10 @@ inline Shape pick_fwd_shape(int64_t rows, int64_t V, int es) {
 // vectors (64 KB bf16) take four vectors per lane of 1024 lanes, all of a
 // lane's loads in flight at once (on 65536 x 32000: selective backward 1.31
 // ms against 1.38 at 1024 x 2, entropy backward 1.36 against 1.47); with few
-// rows (2048 x 32000) 1024 x 4 measured 3% slower.  Longer rows stream two
-// at a time (1024 x 2 was the fastest of 256 x 4/8, 512 x 2/4 and 1024 x 4
-// on 300 KB rows).
+// rows (2048 x 32000) 1024 x 4 measured 3% slower.  Longer rows: 1024 x 2
+// when a row is one workgroup's (the fastest of 256 x 4/8, 512 x 2/4 and
+// 1024 x 4 on 300 KB rows); split_rows below normally cuts them into 64 KB
+// chunks of 1024 x 4 instead.
 inline Shape pick_bwd_shape(int64_t rows, int64_t V, int es) {
   const LaunchOverride o = launch_override(1);
   if (o.wg > 0 && o.unroll > 0) return {o.wg, o.unroll};
@@ -626,18 +640,18 @@ hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s)
 template <typename TIn, typename TOut, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, bool ntl, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false, false>), dim3(unsigned(rows)),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false, false>),
+                       dim3(unsigned(rows * a.nchunk)), dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
 #define X(W, U)                                                                          \
   if (sh.wg == W && sh.unroll == U) {                                                     \
     if (ntl)                                                                              \
       hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, true>),                   \
-                         dim3(unsigned(rows)), dim3(W), 0, s, a);                         \
+                         dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);              \
     else                                                                                  \
       hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, false>),                  \
-                         dim3(unsigned(rows)), dim3(W), 0, s, a);                         \
+                         dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);              \
     return hipGetLastError();                                                             \
   }
     GRPO_SHAPES(X)
@@ -692,10 +706,29 @@ int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
-int launch_bwd(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
+// Rows longer than 4096 vectors (64 KB of bf16) are split over workgroups of
+// 1024 lanes x 4 vectors, one 64 KB chunk each: every workgroup issues all of
+// its loads at once and exits (the whole row per workgroup, 1024 x 2, streamed
+// 300 KB rows at 5.1 TB/s against 6.35 for the same bytes as 64 KB rows).
+// Each chunk recomputes its row's dlogp (a few scalars, or the per-sequence
+// sums).  Without 16-byte rows, or under a launch override, one workgroup per
+// row.
+inline void split_rows(BwdArgs& a, Shape& sh, int64_t rows, int es, bool vec) {
+  a.nchunk = 1;
+  const int64_t nvec = int64_t(a.V) * es / 16;
+  if (!vec || nvec <= 4096 || launch_override(1).wg > 0) return;
+  const int64_t n = (nvec + 4095) / 4096;
+  if (rows * n > (int64_t(1) << 31) - 1) return;
+  sh = {1024, 4};
+  a.nchunk = int(n);
+}
+
+int launch_bwd(const BwdArgs& a0, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
-  const Shape sh = pick_bwd_shape(rows, a.V, es);
-  const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
+  Shape sh = pick_bwd_shape(rows, a0.V, es);
+  const bool vec = rows_vec_ok(a0.logits, a0.ld, es) && rows_vec_ok(a0.dlogits, a0.ld_out, es);
+  BwdArgs a = a0;
+  split_rows(a, sh, rows, es, vec);
   const bool ntl = false;  // same-dtype backward: normal loads measured faster
   hipError_t e;
   if (dtype == GRPO_BF16) e = vec ? launch_bwd_t<uint16_t, uint16_t, true>(a, rows, sh, ntl, s)
@@ -776,14 +809,14 @@ template <typename T>
 hipError_t launch_bwd_entropy_t(const BwdArgs& a, int64_t rows, bool vec, Shape sh,
                                 hipStream_t s) {
   if (!vec) {
-    hipLaunchKernelGGL((row_bwd_kernel<T, T, 256, 4, false, false, true>), dim3(unsigned(rows)),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL((row_bwd_kernel<T, T, 256, 4, false, false, true>),
+                       dim3(unsigned(rows * a.nchunk)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
 #define X(W, U)                                                                          \
   if (sh.wg == W && sh.unroll == U) {                                                     \
-    hipLaunchKernelGGL((row_bwd_kernel<T, T, W, U, true, false, true>), dim3(unsigned(rows)), \
-                       dim3(W), 0, s, a);                                                 \
+    hipLaunchKernelGGL((row_bwd_kernel<T, T, W, U, true, false, true>),                  \
+                       dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);                \
     return hipGetLastError();                                                             \
   }
   X(256, 2)
@@ -795,10 +828,12 @@ hipError_t launch_bwd_entropy_t(const BwdArgs& a, int64_t rows, bool vec, Shape 
 
 // the entropy backward takes the backward's shape rule (256 x 2, 1024 x 4 or
 // 1024 x 2; an override must name one of these)
-int launch_bwd_entropy(const BwdArgs& a, int dtype, int64_t rows, hipStream_t s) {
+int launch_bwd_entropy(const BwdArgs& a0, int dtype, int64_t rows, hipStream_t s) {
   const int es = elem_size(dtype);
-  const bool vec = rows_vec_ok(a.logits, a.ld, es) && rows_vec_ok(a.dlogits, a.ld_out, es);
-  const Shape sh = pick_bwd_shape(rows, a.V, es);
+  const bool vec = rows_vec_ok(a0.logits, a0.ld, es) && rows_vec_ok(a0.dlogits, a0.ld_out, es);
+  Shape sh = pick_bwd_shape(rows, a0.V, es);
+  BwdArgs a = a0;
+  split_rows(a, sh, rows, es, vec);
   const hipError_t e = dtype == GRPO_BF16 ? launch_bwd_entropy_t<uint16_t>(a, rows, vec, sh, s)
                                           : launch_bwd_entropy_t<float>(a, rows, vec, sh, s);
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;

@@ -53,6 +53,7 @@ struct BwdArgs {
   int32_t mode, level, force_dense;
   uint8_t* zero_row;
   const int32_t* dev_rows;  // nullable: rows at or past *dev_rows are skipped
+  int32_t nchunk;           // workgroups per row (set by the launchers, >= 1)
 };
 
 struct SeqArgs {

@@ -80,6 +80,34 @@ def test_entropy_bwd_bf16_strided_and_in_place():
     assert np.array_equal(bits(view), bits(dz))
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 32779), ("f32", 16391)])
+def test_entropy_bwd_split_rows(dtype, V):
+    """Rows of 4097 vectors with a 3-element tail on a 16-byte pitch: the
+    backward takes one workgroup per 64 KB chunk of a row."""
+    lib = require_gpu()
+    say(f"entropy backward {dtype}: 10 x {V} (rows split into chunks)")
+    N, T = 10, 0.8
+    es = 2 if dtype == "bf16" else 4
+    pad = (-V) % (16 // es)
+    rng = np.random.default_rng(V)
+    zf = (rng.standard_normal((N, V + pad)) * 2.0).astype(np.float32)
+    zb = synth.f32_to_bf16_bits(zf) if dtype == "bf16" else zf
+    t = logits_to_dev(zb, dtype)[:, :V]
+    z64 = oracle.to_f64(zb, dtype)[:, :V]
+    g = rng.standard_normal(N).astype(np.float32)
+    g[3] = 0.0
+    lse, H = _entropy_inputs(z64, T)
+    dz = lib.entropy_from_logits_bwd(t, dev(lse.astype(np.float32)), dev(H.astype(np.float32)),
+                                     dev(g), temperature=T)
+    torch.cuda.synchronize()
+    want = oracle.entropy_from_logits_bwd(z64, g.astype(np.float64), T)
+    tol = 1e-5 * np.abs(want) + _entropy_bound(z64, T, g, lse, H) + 1e-30
+    if dtype == "bf16":
+        tol = tol + 2.0 ** -8 * np.abs(want)
+    assert (np.abs(dev_to_f64(dz) - want) <= tol).all()
+    assert (bits(dz)[3] == 0).all()
+
+
 def test_entropy_bwd_ragged_unaligned_rows():
     """V = 1003 bf16: rows not 16-byte aligned take the element-wise path."""
     lib = require_gpu()

@@ -435,6 +435,70 @@ def test_ragged_and_strided_rows(dtype, V, ld_extra):
     assert_rel(H.cpu().numpy(), oracle.entropy_from_logits(z64, 0.9), "entropy")
 
 
+@pytest.mark.parametrize("level", ["token", "sequence"])
+@pytest.mark.parametrize("dtype,V", [("bf16", 32779), ("bf16", 65536), ("f32", 16388),
+                                     ("f32", 16391)])
+def test_split_rows_backward(dtype, V, level):
+    """Rows past 4096 vectors: the backward takes one workgroup per 64 KB
+    chunk.  4097 vectors (the last chunk one vector, with or without a tail
+    of 3 elements) and exactly two chunks; the sampled ids sit on the row's
+    first and last element and on both sides of the chunk boundary; the
+    second sequence has advantage 0 (beta 0: zero rows; the old log-probs
+    close enough that no token of the first is clipped).  Checked against
+    the oracle, the zero rows' flags and +0.0, the forced-dense result equal
+    to the skipping one, the pad columns of a wider output untouched, and
+    rows with an out-of-range id all NaN."""
+    lib = require_gpu()
+    say(f"split rows: dtype {dtype} V={V} level {level}")
+    B, L = 2, 4
+    es = 2 if dtype == "bf16" else 4
+    VE = 16 // es
+    pad = (-V) % VE or VE  # a 16-byte row pitch: the vector path
+    rng = np.random.default_rng(V + (1 if level == "token" else 2))
+    zf = (rng.standard_normal((B * L, V + pad)) * 2.0).astype(np.float32)
+    zb = synth.f32_to_bf16_bits(zf) if dtype == "bf16" else zf
+    t = logits_to_dev(zb, dtype)[:, :V]
+    z64 = oracle.to_f64(zb, dtype)[:, :V]
+    edge = 4096 * VE  # first element of the second chunk
+    ids = rng.integers(0, V, B * L).astype(np.int64)
+    ids[:4] = [0, V - 1, edge - 1, edge]
+    adv = np.array([0.9, 0.0], np.float32)
+    lp, _ = oracle.selective_log_softmax(z64, ids, 0.9)
+    case = synth.GrpoCase(name="split", B=B, L=L, V=V, dtype=dtype, logits=None, ids=ids, adv=adv,
+                          mask=np.ones(B * L, np.uint8), old_noise=rng.standard_normal(B * L) * 0.01,
+                          ref_noise=None, dloss=np.full(B * L, 1.0 / (B * L), np.float32),
+                          temperature=0.9, beta=0.0, eps_low=0.2, eps_high=0.28, level=level)
+    inp = GrpoInputs(case, lp)
+    fwd, dz, zr = run_grpo_gpu(lib, t, inp)
+    o, g = oracle_expectations(inp, z64, fwd)
+    assert (g[4:] == 0.0).all() and (g[:4] != 0.0).all()
+    check_forward(case, o, fwd)
+    check_backward(case, o, g, dz, zr, z64, inp)
+    d = inp.to_dev()
+    kw = dict(ref_logp=None, mask=d["mask"], seq_ratio=fwd.get("seq_ratio"), temperature=0.9,
+              beta=0.0, eps_low=0.2, eps_high=0.28, level=level)
+    dense, _ = lib.grpo_logits_bwd(t, d["ids"], d["old_logp"], d["adv"], B, L, fwd["logp"],
+                                   fwd["lse"], d["dloss"], force_dense=True, **kw)
+    wide = torch.full((B * L, V + pad), float("nan"), dtype=t.dtype, device="cuda")
+    sentinel = wide[:, V:].clone()
+    lib.grpo_logits_bwd(t, d["ids"], d["old_logp"], d["adv"], B, L, fwd["logp"], fwd["lse"],
+                        d["dloss"], dlogits=wide[:, :V], **kw)
+    bad = ids.copy()
+    bad[[1, 2, 5]] = [-1, V, -1]
+    bad_t = dev(bad)
+    nan_dz, _ = lib.grpo_logits_bwd(t, bad_t, d["old_logp"], d["adv"], B, L, fwd["logp"],
+                                    fwd["lse"], d["dloss"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(dense, dz)
+    assert np.array_equal(bits(wide[:, :V]), bits(dz))
+    assert torch.equal(wide[:, V:].view(torch.int16) if es == 2 else wide[:, V:].view(torch.int32),
+                       sentinel.view(torch.int16) if es == 2 else sentinel.view(torch.int32))
+    n = dev_to_f64(nan_dz)
+    assert np.isnan(n[[1, 2, 5]]).all()
+    keep = [0, 3, 4, 6, 7]
+    assert np.array_equal(bits(nan_dz)[keep], bits(dz)[keep])
+
+
 @pytest.mark.parametrize("dtype,V,ld_extra", [("f32", 17, 0), ("bf16", 1003, 0), ("bf16", 1003, 1),
                                              ("bf16", 32000, 0), ("f32", 4099, 5),
                                              ("bf16", 151936, 0)])
