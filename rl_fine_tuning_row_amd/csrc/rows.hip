@@ -2,8 +2,8 @@
 // grpo_logits_fwd, grpo_logits_bwd, entropy_from_logits,
 // selective_log_softmax, selective_log_softmax_bwd.
 //
-// One workgroup per row (the backward splits rows past 64 KB into 64 KB
-// chunks, one workgroup each).  Lanes stream the row with 128-bit loads (8
+// One workgroup per row (the backward splits rows into chunks of 8 or 64 KB,
+// one workgroup each).  Lanes stream the row with 128-bit loads (8
 // bf16 or 4 fp32 per lane), UNROLL vectors in flight per lane, fold each
 // register tile into the online softmax state (row_core.hpp), reduce across
 // the wave with lane shuffles and across waves through LDS, and lane 0 writes
@@ -706,20 +706,30 @@ int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
-// Rows longer than 4096 vectors (64 KB of bf16) are split over workgroups of
-// 1024 lanes x 4 vectors, one 64 KB chunk each: every workgroup issues all of
-// its loads at once and exits (the whole row per workgroup, 1024 x 2, streamed
-// 300 KB rows at 5.1 TB/s against 6.35 for the same bytes as 64 KB rows).
-// Each chunk recomputes its row's dlogp (a few scalars, or the per-sequence
-// sums).  Without 16-byte rows, or under a launch override, one workgroup per
-// row.
+// Rows are split into chunks, one workgroup each, that issue all of their
+// loads at once and exit; each chunk recomputes its row's dlogp.  Where that
+// is a few per-row scalars (token level, selective log-softmax) the chunks
+// are 512 vectors (256 lanes x 2): the headline's two-pass backward 23.7
+// against 26.3 us, the selective backward on 65536 x 32000 1.27 against 1.31
+// ms.  At the sequence level dlogp needs the sequence's sums of dloss and
+// the mask (L loads and a workgroup reduction per chunk), and the entropy
+// backward does more arithmetic per element: there rows past 4096 vectors
+// take 4096-vector chunks (1024 x 4; 512-vector ones made the sequence-level
+// backward 0.70 against 0.54 ms and the entropy backward 11% slower).  The
+// whole row per workgroup, 1024 x 2, streamed 300 KB rows at 5.1 TB/s
+// against 6.35 for the same bytes as 64 KB rows.  Without 16-byte rows, or
+// under a launch override, one workgroup per row.
 inline void split_rows(BwdArgs& a, Shape& sh, int64_t rows, int es, bool vec) {
   a.nchunk = 1;
+  if (!vec || launch_override(1).wg > 0) return;
+  const bool costly = a.mode == BWD_ENTROPY || (a.mode == BWD_GRPO && a.level == GRPO_SEQUENCE);
+  const Shape c = costly ? Shape{1024, 4} : Shape{256, 2};
+  const int64_t cv = int64_t(c.wg) * c.unroll;
   const int64_t nvec = int64_t(a.V) * es / 16;
-  if (!vec || nvec <= 4096 || launch_override(1).wg > 0) return;
-  const int64_t n = (nvec + 4095) / 4096;
+  if (nvec <= cv) return;
+  const int64_t n = (nvec + cv - 1) / cv;
   if (rows * n > (int64_t(1) << 31) - 1) return;
-  sh = {1024, 4};
+  sh = c;
   a.nchunk = int(n);
 }
 

@@ -83,7 +83,7 @@ def test_entropy_bwd_bf16_strided_and_in_place():
 @pytest.mark.parametrize("dtype,V", [("bf16", 32779), ("f32", 16391)])
 def test_entropy_bwd_split_rows(dtype, V):
     """Rows of 4097 vectors with a 3-element tail on a 16-byte pitch: the
-    backward takes one workgroup per 64 KB chunk of a row."""
+    entropy backward takes one workgroup per 4096-vector chunk of a row."""
     lib = require_gpu()
     say(f"entropy backward {dtype}: 10 x {V} (rows split into chunks)")
     N, T = 10, 0.8

@@ -439,10 +439,12 @@ def test_ragged_and_strided_rows(dtype, V, ld_extra):
 @pytest.mark.parametrize("dtype,V", [("bf16", 32779), ("bf16", 65536), ("f32", 16388),
                                      ("f32", 16391)])
 def test_split_rows_backward(dtype, V, level):
-    """Rows past 4096 vectors: the backward takes one workgroup per 64 KB
-    chunk.  4097 vectors (the last chunk one vector, with or without a tail
-    of 3 elements) and exactly two chunks; the sampled ids sit on the row's
-    first and last element and on both sides of the chunk boundary; the
+    """Long rows: the backward takes one workgroup per chunk of a row (512
+    vectors at token level, 4096 at sequence level).  4097 vectors (the last
+    chunk one vector, with or without a tail of 3 elements) and 8192 (whole
+    chunks only); the sampled ids sit on the row's first and last element
+    and on both sides of the 4096-vector boundary (a chunk boundary at both
+    levels); the
     second sequence has advantage 0 (beta 0: zero rows; the old log-probs
     close enough that no token of the first is clipped).  Checked against
     the oracle, the zero rows' flags and +0.0, the forced-dense result equal
