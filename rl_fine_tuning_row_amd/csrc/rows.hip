@@ -407,7 +407,7 @@ __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   const u32x4* __restrict__ rv = reinterpret_cast<const u32x4*>(row);
   const u32x4 fill = {Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits, Fill<TIn>::bits};
 
-  static_assert(WG > 64, "the gathered logit is passed through the reduction's LDS barrier");
+  static_assert(WG >= 64 && (WG & (WG - 1)) == 0, "whole waves, a power of two of them");
   // per-row scalars first: their latency hides under the row's loads
   const int64_t y = f.ids[r];
   const float w = a.dloss[r];
@@ -748,10 +748,10 @@ int launch_bwd(const BwdArgs& a0, int dtype, int64_t rows, hipStream_t s) {
   return e == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }
 
-// Single-pass launch: the row held in registers, 8 16-byte vectors per lane
-// of a 256-lane workgroup up to 2048 vectors, 4 per lane of a 1024-lane one
-// up to 4096, then 16 per lane of 512 lanes; rows longer than 128 KB do not
-// fit.
+// Single-pass launch: the row held in registers, 4 16-byte vectors per lane
+// of one wave up to 256 vectors, 8 per lane of a 256-lane workgroup up to
+// 2048, 4 per lane of a 1024-lane one up to 4096, then 16 per lane of 512
+// lanes; rows longer than 128 KB do not fit.
 // Returns false (nothing launched) when the row does not fit or the rows are
 // not 16-byte aligned.
 template <typename TIn, bool NEED_T>
@@ -762,6 +762,7 @@ hipError_t launch_fused_t(const FusedArgs& a, int64_t rows, int wg, int vpt, hip
                        dim3(W), 0, s, a);                                               \
     return hipGetLastError();                                                           \
   }
+  X(64, 4)
   X(256, 8)
   X(256, 16)
   X(512, 8)
@@ -781,8 +782,12 @@ bool fused_shape(int64_t V, int es, int& wg, int& vpt) {
   }
   // On 64 KB rows (4000 vectors, interleaved rounds on MI355X) 1024 x 4 ran
   // 46.5 us against 47.4 for 512 x 8, 48.8 for 256 x 16 and 51.5 for
-  // 512 x 16; sixteen vectors per lane only for rows past 4096 vectors
-  if (nvec <= 256 * 8) {
+  // 512 x 16; sixteen vectors per lane only for rows past 4096 vectors.
+  // Rows of up to 256 vectors take one wave (no cross-wave merge).
+  if (nvec <= 64 * 4) {
+    wg = 64;
+    vpt = 4;
+  } else if (nvec <= 256 * 8) {
     wg = 256;
     vpt = 8;
   } else if (nvec <= 1024 * 4) {

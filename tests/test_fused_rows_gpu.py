@@ -105,6 +105,18 @@ def test_single_pass_every_shape(shape, dtype, V, monkeypatch):
     _edge_case(lib, dtype, V, 5, 0.9, out_pitch=True)
 
 
+@pytest.mark.parametrize("dtype,V,pad", [("bf16", 2048, 0), ("bf16", 2047, 1), ("f32", 1024, 0),
+                                         ("f32", 1027, 1), ("bf16", 2056, 0), ("f32", 1028, 0)])
+def test_single_pass_one_wave(dtype, V, pad):
+    """Rows of up to 256 vectors take one 64-lane wave with 4 vectors per
+    lane (no cross-wave merge): exactly 256 vectors, 255 plus a 7-element
+    tail and 256 plus a 3-element tail (16-byte pitch V + pad for input and
+    output); 257 vectors take 256 lanes x 8."""
+    lib = require_gpu()
+    say(f"single-pass one wave: {dtype} V={V} ld=V+{pad}")
+    _edge_case(lib, dtype, V, pad, 0.9, out_pitch=pad > 0)
+
+
 @pytest.mark.parametrize("dtype,V", [("bf16", 40), ("bf16", 1003), ("f32", 17), ("f32", 200)])
 @pytest.mark.parametrize("T", [0.05, 0.1, 0.3, 0.5, 0.7, 1.0, 1.3, 2.0, 10.0])
 def test_single_pass_lanes_without_elements(dtype, V, T):
