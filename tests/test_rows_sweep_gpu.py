@@ -69,3 +69,64 @@ def test_row_path_sweep(k):
         o1, g1 = oracle_expectations(inp, z64, one)
         check_forward(case, o1, one, ref=inp.ref)
         check_backward(case, o1, g1, dz1, zr1, z64, inp)
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_entropy_selective_sweep(k):
+    """entropy_from_logits, selective_log_softmax and its backward, and the
+    entropy backward over the same row-length and pitch boundaries.  The
+    backwards take the oracle's lse and H rounded to fp32.  Bars: the
+    forwards as in test_rows_gpu; the selective backward in fp32 within
+    2^-21 |g/T| p (1 + |z|/T + |lse|) + 2^-22 |o| (the exponent's and the
+    product's fp32 roundings, the inputs' rounding included), in bf16 the
+    output rounding's bar; the entropy backward as in test_aux_gpu."""
+    from test_aux_gpu import _entropy_bound
+    from gpu_common import assert_bf16_dz, assert_rel, bits, dev, dev_to_f64
+    import torch
+    lib = require_gpu()
+    rng = np.random.default_rng(2000 + k)
+    dtype = "f32" if k % 2 == 0 else "bf16"
+    es = 4 if dtype == "f32" else 2
+    VE = 16 // es
+    V = int(NVEC[(5 * k) % len(NVEC)] * VE + rng.choice([0, 1, VE - 1]))
+    aligned_pad = (-V) % VE
+    ld_extra = int(rng.choice([aligned_pad, aligned_pad + VE, 1 if aligned_pad != 1 else 3]))
+    N = int(rng.integers(1, 13))
+    T = float(rng.choice([0.6, 1.0, 1.4]))
+    say(f"entropy/selective sweep {k}: {dtype} V={V} ld=V+{ld_extra} N={N} T={T}")
+    zf = (rng.standard_normal((N, V + ld_extra)) * 3.0).astype(np.float32)
+    zb = synth.f32_to_bf16_bits(zf) if dtype == "bf16" else zf
+    t = logits_to_dev(zb, dtype)[:, :V]
+    z64 = oracle.to_f64(zb, dtype)[:, :V]
+    ids = rng.integers(0, V, N).astype(np.int64)
+    g = rng.standard_normal(N).astype(np.float32)
+    g[rng.integers(N)] = 0.0
+    H = lib.entropy_from_logits(t, temperature=T)
+    logp, lse = lib.selective_log_softmax(t, dev(ids), temperature=T)
+    _, lse_o = oracle.log_softmax_stats(z64, T)
+    H_o = oracle.entropy_from_logits(z64, T)
+    lp_o, _ = oracle.selective_log_softmax(z64, ids, T)
+    lse32, H32 = lse_o.astype(np.float32), H_o.astype(np.float32)
+    dz = lib.selective_log_softmax_bwd(t, dev(ids), dev(lse32), dev(g), temperature=T)
+    dzH = lib.entropy_from_logits_bwd(t, dev(lse32), dev(H32), dev(g), temperature=T)
+    torch.cuda.synchronize()
+    assert_rel(H.cpu().numpy(), H_o, "entropy")
+    assert_rel(logp.cpu().numpy(), lp_o, "logp")
+    assert_rel(lse.cpu().numpy(), lse_o, "lse")
+    want = oracle.selective_log_softmax_bwd(z64, ids, g.astype(np.float64), T)
+    got = dev_to_f64(dz)
+    if dtype == "bf16":
+        assert_bf16_dz(got, want)
+    else:
+        p = np.exp(z64 / T - lse_o[:, None])
+        tol = (np.abs(g.astype(np.float64)) / T)[:, None] * p * 2.0 ** -21 * (
+            1 + np.abs(z64) / T + np.abs(lse_o)[:, None]) + 2.0 ** -22 * np.abs(want) + 1e-30
+        assert (np.abs(got - want) <= tol).all(), np.abs(got - want).max()
+    assert (bits(dz)[g == 0.0] == 0).all()
+    wantH = oracle.entropy_from_logits_bwd(z64, g.astype(np.float64), T)
+    tolH = 1e-5 * np.abs(wantH) + _entropy_bound(z64, T, g, lse_o, H_o) + 1e-30
+    if dtype == "bf16":
+        tolH = tolH + 2.0 ** -8 * np.abs(wantH)
+    errH = np.abs(dev_to_f64(dzH) - wantH)
+    assert (errH <= tolH).all(), errH.max()
+    assert (bits(dzH)[g == 0.0] == 0).all()
