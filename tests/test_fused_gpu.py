@@ -476,3 +476,38 @@ def test_fused_all_rows_zero_weight():
     assert float(loss.item()) == 1.25
     assert (gh.cpu().numpy() == 0.0).all()
     assert np.array_equal(gW.cpu().numpy(), gW0)
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_fused_sweep(k):
+    """A seeded sweep of the fused chunk over small shapes: 1-6 sequences of
+    1-130 tokens (half of them padding on average, so the kept-row count and
+    its rounding up to 64 vary), H of 64-320, V of 8-4104 (ragged last
+    tiles), every chunk size from 1 to B, temperatures 0.6-1.3, token-sum
+    and token-mean weights.  The loss against the oracle within 1e-5
+    relative, every gradient element within the bound of the module doc,
+    exact zero grad_hidden rows where dlogp is 0."""
+    lib = require_gpu()
+    rng = np.random.default_rng(3000 + k)
+    B = int(rng.integers(1, 7))
+    L = int(rng.choice([1, 7, 24, 65, 130]))
+    H = int(rng.choice([64, 128, 192, 320]))
+    V = int(rng.choice([8, 136, 264, 392, 520, 1032, 2056, 4104]))
+    chunk = int(rng.integers(1, B + 1))
+    kind = str(rng.choice(["sum", "mean"]))
+    case = fill_dloss(synth.fused_case(seed=k, B=B, L=L, H=H, V=V, dloss=kind))
+    case.temperature = float(rng.choice([0.6, 0.9, 1.3]))
+    say(f"fused sweep {k}: B={B} L={L} H={H} V={V} chunk={chunk} T={case.temperature} {kind}")
+    h = oracle.decode_bf16(case.hidden)
+    W = oracle.decode_bf16(case.weight)
+    logp_true, _ = oracle.selective_log_softmax(h @ W.T, case.ids, case.temperature)
+    old, ref = _fused_inputs(case, logp_true)
+    loss, gh, gW = _run_fused(lib, case, old, ref, chunk)
+    l_o, _, _ = oracle.fused_linear_grpo(h, W, case.ids, old.astype(np.float64),
+                                         ref.astype(np.float64), case.adv, case.mask,
+                                         case.dloss, case.B, case.L, case.temperature,
+                                         case.beta, case.eps_low, case.eps_high, chunk)
+    assert abs(loss - l_o) <= 1e-5 * abs(l_o) + 1e-6, (loss, l_o)
+    chunks = (case.B + chunk - 1) // chunk
+    g = _check_fused_elementwise(case, h, W, old, ref, gh, gW.cpu().numpy(), chunks)
+    assert (gh[g == 0.0] == 0.0).all()
