@@ -370,3 +370,22 @@ def test_fused_linear_chunk_invariance_and_composition():
                                     case.eps_high)
     np.testing.assert_allclose(gh1, dz @ W, atol=1e-14)
     np.testing.assert_allclose(gW1, dz.T @ h, atol=1e-14)
+
+
+def test_ppo_clip_truth_table():
+    """The clipped surrogate's four quadrants, a ratio inside the interval and
+    a zero advantage, with eps_low 0.2 and eps_high 0.28 (interval [0.8,
+    1.28]); expected loss and clip flag worked out by hand from
+    pg = -min(r A, clip(r) A):
+      r 1.5, A  2: min(3.0, 2.56)   -> pg -2.56, clipped
+      r 0.5, A  2: min(1.0, 1.6)    -> pg -1.0,  not clipped
+      r 0.5, A -2: min(-1.0, -1.6)  -> pg  1.6,  clipped
+      r 1.5, A -2: min(-3.0, -2.56) -> pg  3.0,  not clipped
+      r 1.1, A  2: both 2.2         -> pg -2.2,  not clipped (a tie keeps the gradient)
+      r 1.5, A  0: both 0           -> pg  0,    not clipped"""
+    r = np.array([1.5, 0.5, 0.5, 1.5, 1.1, 1.5])
+    A = np.array([2.0, 2.0, -2.0, -2.0, 2.0, 0.0])
+    ratio, pg, clipped = oracle.ppo_clip_terms(np.log(r), A, 0.2, 0.28)
+    assert np.allclose(ratio, r, rtol=1e-15, atol=0)
+    assert np.allclose(pg, [-2.56, -1.0, 1.6, 3.0, -2.2, 0.0], rtol=1e-14, atol=1e-15)
+    assert clipped.tolist() == [True, False, True, False, False, False]
