@@ -220,3 +220,65 @@ def test_no_fallback_without_the_library():
     assert r.returncode == 0, r.stderr[-2000:]
     assert "RAISED True" in r.stdout and "CALL RAISED" in r.stdout, r.stdout
     assert "LOADED" not in r.stdout and "COMPUTED" not in r.stdout
+
+
+def test_grpo_fwd_bwd_validation(L):
+    """The single-pass entry point: token level only, the in-place and
+    stride rules of the backward, and its own required outputs."""
+    f = L.grpo_logits_fwd_bwd
+    p = _params()
+
+    def call(dtype=1, p=p, dloss=FAKE, loss=FAKE, out=FAKE, ld_out=100, logits=FAKE):
+        return f(logits, dtype, 2, 4, 100, 100, FAKE, FAKE, None, FAKE, None, ctypes.byref(p),
+                 dloss, loss, FAKE, FAKE, None, None, None, out, ld_out, None, None, None)
+    assert call(p=_params(level=1)) == PARAM            # sequence level has no single pass
+    assert call(dtype=3) == DTYPE
+    assert call(ld_out=99) == STRIDE
+    assert call(out=FAKE, ld_out=104) == STRIDE          # in place (same pointer), other stride
+    assert call(dloss=None) == NULL and call(loss=None) == NULL and call(out=None) == NULL
+    assert call(out=ctypes.c_void_p(0x20001)) == ALIGN   # bf16 gradient at an odd byte
+    assert call(loss=FAKE_ODD) == ALIGN
+
+
+def test_gemm_validation(L):
+    """The exported product: operand layouts, the 16-byte chunk rules of its
+    contiguous extents and leading dimensions, and pointer alignment."""
+    g = L.grpo_gemm_bf16
+    A16 = ctypes.c_void_p(0x100000)
+
+    def call(A=A16, al=0, lda=64, B=A16, bl=0, ldb=64, C=A16, ldc=256, M=100, N=256, K=64, acc=0):
+        return g(A, al, lda, B, bl, ldb, C, ldc, M, N, K, acc, None)
+    assert call(M=0) == OK and call(N=0) == OK
+    assert call(C=None) == NULL and call(B=None) == NULL
+    assert call(al=2) == PARAM and call(bl=-1) == PARAM and call(acc=2) == PARAM
+    assert call(K=60, lda=64, ldb=64) == SHAPE           # K not whole 16-byte chunks
+    assert call(al=1, lda=104, M=100) == SHAPE           # M-contiguous A needs M % 8 == 0
+    assert call(bl=1, ldb=256, N=250, ldc=256) == SHAPE  # N-contiguous B needs N % 8 == 0
+    assert call(lda=68) == STRIDE and call(ldb=60) == STRIDE and call(ldc=255) == STRIDE
+    assert call(al=1, lda=96, M=104) == STRIDE           # ld below the contiguous extent
+    assert call(A=ctypes.c_void_p(0x100008)) == ALIGN and call(C=FAKE_ODD) == ALIGN
+    assert call(K=-8) == SHAPE
+
+
+def test_fused_chunk_validation(L):
+    """The chunked fused-linear loss with a caller workspace: too small a
+    workspace, a missing or misaligned one, and the loss settings it does
+    not support (sequence level, the dense-backward flag)."""
+    f = L.fused_linear_grpo_chunk
+    A16 = ctypes.c_void_p(0x100000)
+    need = L.fused_linear_grpo_workspace_bytes(32, 256, 64)
+    assert need > 0
+
+    def call(ws=A16, nbytes=need, params=GrpoParams(0.9, 0.04, 0.2, 0.28, 0, 0), nseq=2, H=64,
+             grad_hidden=A16):
+        return f(A16, nseq, 16, H, A16, 256, A16, A16, None, A16, None, A16,
+                 ctypes.byref(params), A16, grad_hidden, A16, ws, nbytes, None)
+    assert call(nbytes=need - 1) == WORKSPACE
+    assert call(nbytes=0) == WORKSPACE
+    assert call(ws=None) == NULL
+    assert call(ws=ctypes.c_void_p(0x100010)) == ALIGN   # workspace needs 256-byte alignment
+    assert call(grad_hidden=ctypes.c_void_p(0x100004)) == ALIGN
+    assert call(params=GrpoParams(0.9, 0.04, 0.2, 0.28, 0, 1)) == PARAM   # force-dense flag
+    assert call(params=GrpoParams(0.9, 0.04, 0.2, 0.28, 1, 0)) == PARAM   # sequence level
+    assert call(H=0) == SHAPE and call(nseq=-1) == SHAPE
+    assert call(nseq=0, ws=None, nbytes=0) == OK          # empty chunk: nothing to do
