@@ -49,8 +49,12 @@
  *    layouts take an element-wise path with the same results.
  *  - Aliasing: dlogits may alias logits only with the same dtype and
  *    ld_out == ld (in place).  No other output may alias an input.
- *  - Limits: shapes whose launches would need more than 2^31 - 1
- *    workgroups in one grid dimension return GRPO_ERR_SHAPE.
+ *  - Limits: up to 2^31 - 1 rows and 2^26 columns per call.  A dispatch
+ *    covers at most 2^32 - 1 work-items, so the row kernels (and the fused
+ *    chunk's row gather and split-K reduction) run as several launches where
+ *    a call needs more; the matrix products, whose tiles cannot be split
+ *    that way, return GRPO_ERR_SHAPE past 2^32 - 1 work-items (16777215
+ *    tiles of 256 lanes).
  *  - Thread safety: reentrant; every call may run from any host thread.
  *    The row kernels keep no state.  The exception is fused_linear_grpo_chunk,
  *    which keeps one side stream per device for the process (default

@@ -7,6 +7,7 @@
 #include "host_common.hpp"
 
 using grpo::aligned;
+using grpo::groups_per_launch;
 
 namespace {
 
@@ -64,8 +65,8 @@ __global__ __launch_bounds__(1024) void weights_token_kernel(const uint8_t* __re
 // one workgroup per sequence
 __global__ __launch_bounds__(256) void weights_seq_kernel(const uint8_t* __restrict__ mask,
                                                           int64_t B, int L, int per_sequence,
-                                                          float* __restrict__ w) {
-  const int64_t b = blockIdx.x;
+                                                          int64_t b0, float* __restrict__ w) {
+  const int64_t b = b0 + blockIdx.x;
   const uint8_t* m = mask == nullptr ? nullptr : mask + b * L;
   float v;
   if (per_sequence) {
@@ -116,7 +117,11 @@ extern "C" int grpo_loss_weights(const uint8_t* mask, int64_t B, int64_t L, int 
   if (reduction == GRPO_REDUCE_TOKEN)
     hipLaunchKernelGGL(weights_token_kernel, dim3(1), dim3(1024), 0, s, mask, B * L, dloss);
   else
-    hipLaunchKernelGGL(weights_seq_kernel, dim3(unsigned(B)), dim3(256), 0, s, mask, B, int(L),
-                       reduction == GRPO_REDUCE_SEQUENCE ? 1 : 0, dloss);
+    for (int64_t b0 = 0, step = groups_per_launch(256); b0 < B; b0 += step) {
+      hipLaunchKernelGGL(weights_seq_kernel, dim3(unsigned(B - b0 < step ? B - b0 : step)),
+                         dim3(256), 0, s, mask, B, int(L), reduction == GRPO_REDUCE_SEQUENCE ? 1 : 0,
+                         b0, dloss);
+      if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
+    }
   return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
 }

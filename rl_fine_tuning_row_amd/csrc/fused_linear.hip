@@ -196,8 +196,8 @@ __global__ __launch_bounds__(1024) void zero_pad_rows_kernel(const int32_t* __re
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ h, int H,
                                                           const int32_t* __restrict__ map,
                                                           const int32_t* __restrict__ count,
-                                                          uint16_t* __restrict__ h_c) {
-  const int i = blockIdx.x;
+                                                          int64_t i0, uint16_t* __restrict__ h_c) {
+  const int64_t i = i0 + blockIdx.x;
   if (i >= *count) return;
   const uint4* src = reinterpret_cast<const uint4*>(h + int64_t(map[i]) * H);
   uint4* dst = reinterpret_cast<uint4*>(h_c + int64_t(i) * H);
@@ -228,9 +228,9 @@ __global__ __launch_bounds__(1024) void weighted_sum_kernel(const float* __restr
 __global__ __launch_bounds__(256) void splitk_scatter_kernel(const float* __restrict__ part,
                                                              int splits, int64_t stride,
                                                              const int32_t* __restrict__ pos,
-                                                             int64_t R, int H,
+                                                             int64_t R, int H, int64_t e0,
                                                              float* __restrict__ out) {
-  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t e = e0 + (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (e >= R * H) return;
   const int64_t r = e / H;
   const int c = int(e % H);
@@ -258,14 +258,14 @@ int check_fused(const void* hidden, int64_t nseq, int64_t L, int64_t H, const vo
   if (H % 64 != 0 || H > 65536 || V % 8 != 0 || V > (int64_t(1) << 30)) return GRPO_ERR_SHAPE;
   if (nseq > (int64_t(1) << 30) / L) return GRPO_ERR_SHAPE;
   {
-    // launch sizes: the grad_hidden scatter grid (R H / 1024) and the products'
-    // tile counts (128 x 128 tiles, K-splits included) must fit a 31-bit grid
+    // launch sizes: each product's tile grid (128 x 128 tiles at the
+    // smallest, 256 lanes each; K-splits go in the second grid dimension)
+    // must fit one dispatch's 32-bit work-item count
     const int64_t R = nseq * L;
-    const int64_t lim = (int64_t(1) << 31) - 1;
-    if (R * H / 1024 > lim) return GRPO_ERR_SHAPE;
+    const int64_t lim = groups_per_launch(256);
     if (((R + 127) / 128) * ((V + 127) / 128) > lim) return GRPO_ERR_SHAPE;
     if (((V + 127) / 128) * ((H + 127) / 128) > lim) return GRPO_ERR_SHAPE;
-    if (((R + 127) / 128) * ((H + 127) / 128) * 16 > lim) return GRPO_ERR_SHAPE;
+    if (((R + 127) / 128) * ((H + 127) / 128) > lim) return GRPO_ERR_SHAPE;
   }
   const int st = check_params(p);
   if (st != GRPO_OK) return st;
@@ -341,8 +341,9 @@ int fused_chunk_run(const void* hidden, int64_t nseq, int64_t L, int64_t H, cons
   // 0. the rows that carry weight, and their inputs
   hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, s, int(R), int(L), dloss, ids,
                      old_logp, ref_logp, adv, map, pos, cnt, ids_c, old_c, ref_c, adv_c, w_c);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(unsigned(R)), dim3(256), 0, s, h, int(H), map, cnt,
-                     h_c);
+  for (int64_t i0 = 0, step = groups_per_launch(256); i0 < R; i0 += step)
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(unsigned(R - i0 < step ? R - i0 : step)), dim3(256),
+                       0, s, h, int(H), map, cnt, i0, h_c);
   hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(63), dim3(1024), 0, s, cnt, z, int64_t(V), int(V),
                      h_c, int(H));
   if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
@@ -472,9 +473,13 @@ int fused_chunk_run(const void* hidden, int64_t nseq, int64_t L, int64_t H, cons
     status = GRPO_ERR_LAUNCH;
   if (status == GRPO_OK) {
     const int64_t n = R * H;
-    hipLaunchKernelGGL(splitk_scatter_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0,
-                       s, part, w.splits, n, pos, R, int(H), grad_hidden);
-    if (hipGetLastError() != hipSuccess) status = GRPO_ERR_LAUNCH;
+    const int64_t groups = (n / 4 + 255) / 256, step = groups_per_launch(256);
+    for (int64_t g0 = 0; g0 < groups && status == GRPO_OK; g0 += step) {
+      hipLaunchKernelGGL(splitk_scatter_kernel,
+                         dim3(unsigned(groups - g0 < step ? groups - g0 : step)), dim3(256), 0, s,
+                         part, w.splits, n, pos, R, int(H), g0 * 1024, grad_hidden);
+      if (hipGetLastError() != hipSuccess) status = GRPO_ERR_LAUNCH;
+    }
   }
   // the caller's stream waits for the side stream before anything after this
   // call (also after a failed launch: nothing may stay behind unordered)

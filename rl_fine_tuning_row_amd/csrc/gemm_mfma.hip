@@ -813,8 +813,9 @@ extern "C" int grpo_gemm_bf16(const void* A, int a_layout, int64_t lda, const vo
                               int64_t N, int64_t K, int accumulate, void* stream) {
   if (M < 0 || N < 0 || K < 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return GRPO_ERR_SHAPE;
-  // the grid (128 x 128 tiles at most) must fit 31 bits
-  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  // the grid (128 x 128 tiles at the smallest, 256 lanes each) must fit one
+  // dispatch's 32-bit work-item count
+  if (((M + 127) / 128) * ((N + 127) / 128) > groups_per_launch(256)) return GRPO_ERR_SHAPE;
   if (M == 0 || N == 0) return GRPO_OK;
   if (A == nullptr || B == nullptr || C == nullptr) return GRPO_ERR_NULL;
   if ((a_layout != 0 && a_layout != 1) || (b_layout != 0 && b_layout != 1) ||
@@ -852,7 +853,7 @@ extern "C" int grpo_gemm_bf16_logits(const void* A, int64_t lda, const void* B, 
                                      float* zy, void* stream) {
   if (M < 0 || N < 0 || K < 0 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return GRPO_ERR_SHAPE;
-  if (((M + 255) / 256) * ((N + 255) / 256) > (int64_t(1) << 31) - 1) return GRPO_ERR_SHAPE;
+  if (((M + 255) / 256) * ((N + 255) / 256) > groups_per_launch(256)) return GRPO_ERR_SHAPE;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return GRPO_ERR_PARAM;
   if (M == 0 || N == 0) return GRPO_OK;
   if (A == nullptr || B == nullptr || ids == nullptr || z16 == nullptr || stat == nullptr ||

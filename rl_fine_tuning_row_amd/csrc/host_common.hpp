@@ -11,7 +11,15 @@
 namespace grpo {
 
 constexpr int64_t kMaxV = int64_t(1) << 26;        // row length limit (int32 lane indexing)
-constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // one workgroup per row
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1; // rows per call
+
+// A dispatch packet holds each grid dimension in work-items as a 32-bit
+// number, so one launch covers at most 2^32 - 1 work-items (4194303
+// workgroups of 1024 lanes).  Launchers of grids that can be larger (one or
+// more workgroups per row, per sequence or per hidden row) cut them into
+// slices of whole workgroups and pass each slice's first index.
+constexpr int64_t kMaxLaunchItems = (int64_t(1) << 32) - 1;
+inline int64_t groups_per_launch(int threads) { return kMaxLaunchItems / threads; }
 
 inline int elem_size(int dtype) { return dtype == GRPO_BF16 ? 2 : 4; }
 

@@ -124,7 +124,7 @@ __device__ __forceinline__ void fwd_token_epilogue(const FwdArgs& a, int64_t r, 
 
 template <typename TIn, int WG, int UNROLL, bool VEC, bool NEED_T, bool NTL>
 __global__ __launch_bounds__(WG) void row_fwd_kernel(FwdArgs a) {
-  const int64_t r = blockIdx.x;
+  const int64_t r = a.row0 + blockIdx.x;
   if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const TIn* __restrict__ row = static_cast<const TIn*>(a.logits) + r * a.ld;
   const Stat st = block_reduce_stat<WG, NEED_T>(
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
                                                                     int64_t rows) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rl = lane >> 2, sub = lane & 3;
-  const int64_t r = int64_t(blockIdx.x) * kPartialRows + rl;
+  const int64_t r = a.row0 + int64_t(blockIdx.x) * kPartialRows + rl;
   const int64_t R = a.dev_rows != nullptr ? min(rows, int64_t(*a.dev_rows)) : rows;
   Stat st;
   stat_init(st);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * NW) void row_fwd_partials_kernel(FwdArgs a,
 // sequence level: one workgroup per sequence; mask-weighted mean log-ratio,
 // one clipped ratio per sequence, pg broadcast to the sequence's tokens.
 __global__ __launch_bounds__(256) void seq_fwd_epilogue_kernel(SeqArgs a) {
-  const int64_t b = blockIdx.x;
+  const int64_t b = a.b0 + blockIdx.x;
   const int64_t base = b * a.L;
   float sx = 0.0f, sm = 0.0f;
   for (int t = threadIdx.x; t < a.L; t += 256) {
@@ -282,8 +282,9 @@ template <typename TIn, typename TOut, int WG, int UNROLL, bool VEC, bool NTL, b
 __global__ __launch_bounds__(WG) void row_bwd_kernel(BwdArgs a) {
   // a.nchunk workgroups per row, each on WG * UNROLL consecutive vectors (the
   // last one on the rest of the row and its tail elements)
-  const int64_t r = int64_t(blockIdx.x) / a.nchunk;
-  const int ch = int(int64_t(blockIdx.x) - r * a.nchunk);
+  const int64_t rl = int64_t(blockIdx.x) / a.nchunk;
+  const int ch = int(int64_t(blockIdx.x) - rl * a.nchunk);
+  const int64_t r = a.row0 + rl;
   const bool last = ch == a.nchunk - 1;
   if (a.dev_rows != nullptr && r >= *a.dev_rows) return;
   const float g = uniform(row_dlogp<TIn, WG>(a, r));
@@ -397,7 +398,7 @@ __device__ __forceinline__ void keep_packed(u32x4& v) { asm volatile("" : "+v"(v
 template <typename TIn, int WG, int VPT, bool NEED_T>
 __global__ __launch_bounds__(WG) void row_fused_kernel(FusedArgs a) {
   constexpr int VE = Vec<TIn>::N;
-  const int64_t r = blockIdx.x;
+  const int64_t r = a.f.row0 + blockIdx.x;
   const int tid = threadIdx.x;
   const FwdArgs& f = a.f;
   const TIn* __restrict__ row = static_cast<const TIn*>(f.logits) + r * f.ld;
@@ -618,19 +619,37 @@ inline Shape pick_bwd_shape(int64_t rows, int64_t V, int es) {
   X(1024, 2)           \
   X(1024, 4)
 
+inline void set_row0(FwdArgs& a, int64_t r0) { a.row0 = r0; }
+inline void set_row0(BwdArgs& a, int64_t r0) { a.row0 = r0; }
+inline void set_row0(FusedArgs& a, int64_t r0) { a.f.row0 = r0; }
+
+// Launch kernel k over `rows` rows, `per` workgroups of `threads` lanes
+// each per row, in as many launches as one dispatch's 32-bit work-item count
+// requires (each launch told its first row).
+template <typename Args>
+hipError_t launch_row_slices(void (*k)(Args), Args a, int64_t rows, int64_t per, int threads,
+                             hipStream_t s) {
+  const int64_t step = groups_per_launch(threads) / per;
+  if (step < 1) return hipErrorInvalidConfiguration;
+  for (int64_t r0 = 0; r0 < rows; r0 += step) {
+    set_row0(a, r0);
+    const int64_t n = rows - r0 < step ? rows - r0 : step;
+    hipLaunchKernelGGL(k, dim3(unsigned(n * per)), dim3(threads), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename TIn, bool VEC, bool NEED_T, bool NTL>
 hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_fwd_kernel<TIn, 256, 4, false, NEED_T, false>),
-                       dim3(unsigned(rows)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_row_slices(row_fwd_kernel<TIn, 256, 4, false, NEED_T, false>, a, rows, 1, 256,
+                             s);
   } else {
 #define X(W, U)                                                                          \
-  if (sh.wg == W && sh.unroll == U) {                                                     \
-    hipLaunchKernelGGL((row_fwd_kernel<TIn, W, U, true, NEED_T, NTL>),                    \
-                       dim3(unsigned(rows)), dim3(W), 0, s, a);                           \
-    return hipGetLastError();                                                             \
-  }
+  if (sh.wg == W && sh.unroll == U)                                                       \
+    return launch_row_slices(row_fwd_kernel<TIn, W, U, true, NEED_T, NTL>, a, rows, 1, W, s);
     GRPO_SHAPES(X)
 #undef X
     return hipErrorInvalidConfiguration;
@@ -640,20 +659,15 @@ hipError_t launch_fwd_t(const FwdArgs& a, int64_t rows, Shape sh, hipStream_t s)
 template <typename TIn, typename TOut, bool VEC>
 hipError_t launch_bwd_t(const BwdArgs& a, int64_t rows, Shape sh, bool ntl, hipStream_t s) {
   if constexpr (!VEC) {
-    hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, 256, 4, false, false>),
-                       dim3(unsigned(rows * a.nchunk)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_row_slices(row_bwd_kernel<TIn, TOut, 256, 4, false, false>, a, rows, a.nchunk,
+                             256, s);
   } else {
 #define X(W, U)                                                                          \
-  if (sh.wg == W && sh.unroll == U) {                                                     \
-    if (ntl)                                                                              \
-      hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, true>),                   \
-                         dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);              \
-    else                                                                                  \
-      hipLaunchKernelGGL((row_bwd_kernel<TIn, TOut, W, U, true, false>),                  \
-                         dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);              \
-    return hipGetLastError();                                                             \
-  }
+  if (sh.wg == W && sh.unroll == U)                                                       \
+    return ntl ? launch_row_slices(row_bwd_kernel<TIn, TOut, W, U, true, true>, a, rows,  \
+                                   a.nchunk, W, s)                                        \
+               : launch_row_slices(row_bwd_kernel<TIn, TOut, W, U, true, false>, a, rows, \
+                                   a.nchunk, W, s);
     GRPO_SHAPES(X)
 #undef X
     return hipErrorInvalidConfiguration;
@@ -700,10 +714,17 @@ int launch_fwd_partials(const FwdArgs& a, const float* stat, int P, int64_t stat
                         const float* zy, int64_t rows, hipStream_t s) {
   if (rows <= 0) return GRPO_OK;
   constexpr int NW = 16;
-  hipLaunchKernelGGL((row_fwd_partials_kernel<NW>),
-                     dim3(unsigned((rows + kPartialRows - 1) / kPartialRows)), dim3(64 * NW), 0, s,
-                     a, stat, P, stat_ld, zy, rows);
-  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+  const int64_t step = groups_per_launch(64 * NW) * kPartialRows;
+  FwdArgs b = a;
+  for (int64_t r0 = 0; r0 < rows; r0 += step) {
+    b.row0 = r0;
+    const int64_t n = rows - r0 < step ? rows - r0 : step;
+    hipLaunchKernelGGL((row_fwd_partials_kernel<NW>),
+                       dim3(unsigned((n + kPartialRows - 1) / kPartialRows)), dim3(64 * NW), 0, s,
+                       b, stat, P, stat_ld, zy, rows);
+    if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
+  }
+  return GRPO_OK;
 }
 
 // Rows are split into chunks, one workgroup each, that issue all of their
@@ -728,7 +749,6 @@ inline void split_rows(BwdArgs& a, Shape& sh, int64_t rows, int es, bool vec) {
   const int64_t nvec = int64_t(a.V) * es / 16;
   if (nvec <= cv) return;
   const int64_t n = (nvec + cv - 1) / cv;
-  if (rows * n > (int64_t(1) << 31) - 1) return;
   sh = c;
   a.nchunk = int(n);
 }
@@ -757,11 +777,8 @@ int launch_bwd(const BwdArgs& a0, int dtype, int64_t rows, hipStream_t s) {
 template <typename TIn, bool NEED_T>
 hipError_t launch_fused_t(const FusedArgs& a, int64_t rows, int wg, int vpt, hipStream_t s) {
 #define X(W, P)                                                                        \
-  if (wg == W && vpt == P) {                                                            \
-    hipLaunchKernelGGL((row_fused_kernel<TIn, W, P, NEED_T>), dim3(unsigned(rows)),     \
-                       dim3(W), 0, s, a);                                               \
-    return hipGetLastError();                                                           \
-  }
+  if (wg == W && vpt == P)                                                              \
+    return launch_row_slices(row_fused_kernel<TIn, W, P, NEED_T>, a, rows, 1, W, s);
   X(64, 4)
   X(256, 8)
   X(256, 16)
@@ -823,17 +840,13 @@ int launch_fused(const FusedArgs& a, int dtype, int64_t rows, bool need_t, bool&
 template <typename T>
 hipError_t launch_bwd_entropy_t(const BwdArgs& a, int64_t rows, bool vec, Shape sh,
                                 hipStream_t s) {
-  if (!vec) {
-    hipLaunchKernelGGL((row_bwd_kernel<T, T, 256, 4, false, false, true>),
-                       dim3(unsigned(rows * a.nchunk)), dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
+  if (!vec)
+    return launch_row_slices(row_bwd_kernel<T, T, 256, 4, false, false, true>, a, rows, a.nchunk,
+                             256, s);
 #define X(W, U)                                                                          \
-  if (sh.wg == W && sh.unroll == U) {                                                     \
-    hipLaunchKernelGGL((row_bwd_kernel<T, T, W, U, true, false, true>),                  \
-                       dim3(unsigned(rows * a.nchunk)), dim3(W), 0, s, a);                \
-    return hipGetLastError();                                                             \
-  }
+  if (sh.wg == W && sh.unroll == U)                                                       \
+    return launch_row_slices(row_bwd_kernel<T, T, W, U, true, false, true>, a, rows, a.nchunk, \
+                             W, s);
   X(256, 2)
   X(1024, 2)
   X(1024, 4)
@@ -939,8 +952,14 @@ extern "C" int grpo_logits_fwd(const void* logits, int dtype, int64_t B, int64_t
   q.loss = loss;
   q.is_clipped = is_clipped;
   q.seq_ratio = seq_ratio;
-  hipLaunchKernelGGL(seq_fwd_epilogue_kernel, dim3(unsigned(B)), dim3(256), 0, s, q);
-  return hipGetLastError() == hipSuccess ? GRPO_OK : GRPO_ERR_LAUNCH;
+  const int64_t step = groups_per_launch(256);
+  for (int64_t b0 = 0; b0 < B; b0 += step) {
+    q.b0 = b0;
+    hipLaunchKernelGGL(seq_fwd_epilogue_kernel, dim3(unsigned(B - b0 < step ? B - b0 : step)),
+                       dim3(256), 0, s, q);
+    if (hipGetLastError() != hipSuccess) return GRPO_ERR_LAUNCH;
+  }
+  return GRPO_OK;
 }
 
 extern "C" int grpo_logits_bwd(const void* logits, int dtype, int64_t B, int64_t L, int64_t V,

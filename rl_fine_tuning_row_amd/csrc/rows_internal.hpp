@@ -30,6 +30,7 @@ struct FwdArgs {
   float* gathered;
   int32_t* err_count;
   const int32_t* dev_rows;  // nullable: rows at or past *dev_rows are skipped
+  int64_t row0;             // first row of this launch (set by the launchers)
 };
 
 struct BwdArgs {
@@ -54,6 +55,7 @@ struct BwdArgs {
   uint8_t* zero_row;
   const int32_t* dev_rows;  // nullable: rows at or past *dev_rows are skipped
   int32_t nchunk;           // workgroups per row (set by the launchers, >= 1)
+  int64_t row0;             // first row of this launch (set by the launchers)
 };
 
 struct SeqArgs {
@@ -66,6 +68,7 @@ struct SeqArgs {
   float* loss;
   uint8_t* is_clipped;
   float* seq_ratio;
+  int64_t b0;  // first sequence of this launch
 };
 
 // Launch the forward-type row kernel (GRPO / entropy / selective
