@@ -44,6 +44,10 @@ def test_entropy_validation(L):
     assert e(FAKE, 1, 10, 100, 100, float("nan"), FAKE, None) == PARAM
     assert e(FAKE_ODD, 0, 10, 100, 100, 1.0, FAKE, None) == ALIGN
     assert e(FAKE, 1, 0, 100, 100, 1.0, None, None) == OK   # empty: no-op, nothing touched
+    big = 1 << 26                                            # the longest row accepted
+    assert e(FAKE, 1, 0, big, big, 1.0, None, None) == OK
+    assert e(FAKE, 1, 10, big + 1, big + 1, 1.0, FAKE, None) == SHAPE
+    assert e(FAKE, 1, (1 << 31), 8, 8, 1.0, FAKE, None) == SHAPE   # rows past 2^31 - 1
 
 
 def test_selective_validation(L):

@@ -43,7 +43,7 @@ BWD_STEP = ITEMS // 256   # rows per backward launch; sequences per epilogue lau
 T, EPS_LOW, EPS_HIGH = 0.9, 0.2, 0.28
 
 
-def _draw(B, L, seed):
+def _draw(B, L, seed, V=V):
     g = torch.Generator(device="cuda").manual_seed(seed)
     N = B * L
     dv = dict(device="cuda", generator=g)
@@ -101,7 +101,7 @@ def _sub_inputs(d, seqs, L, level, beta):
     host = lambda t, i: t.index_select(0, i).cpu().numpy()
     z_bits = d["z"].index_select(0, ri).view(torch.int16).cpu().numpy().view(np.uint16)
     c = types.SimpleNamespace(
-        B=len(seqs), L=L, N=len(rows), V=V, level=level, beta=beta, temperature=T,
+        B=len(seqs), L=L, N=len(rows), V=d["z"].shape[1], level=level, beta=beta, temperature=T,
         eps_low=EPS_LOW, eps_high=EPS_HIGH, ids=host(d["ids"], ri), adv=host(d["adv"], si),
         mask=host(d["mask"], ri), dloss=host(d["dloss"], ri))
     inp = GrpoInputs.__new__(GrpoInputs)
@@ -122,6 +122,45 @@ def _grpo_outputs(N, B, level, with_gathered=True):
 def _pick(outs, ri, si):
     return {k: (v.index_select(0, si) if k == "seq_ratio" else v.index_select(0, ri))
             for k, v in outs.items()}
+
+
+def _entropy_selective(lib, d, N):
+    """entropy_from_logits, selective_log_softmax and both backwards on the
+    whole of d, into sentinel-filled outputs; the backwards take the
+    forwards' lse and H."""
+    V_ = d["z"].shape[1]
+    H = lib.entropy_from_logits(d["z"], T, out=_sentinel(N))
+    lp, lse = lib.selective_log_softmax(d["z"], d["ids"], T, out=_sentinel(N), lse=_sentinel(N))
+    sdz = lib.selective_log_softmax_bwd(d["z"], d["ids"], lse, d["grad"], T,
+                                        dlogits=_sentinel(N, torch.bfloat16, (N, V_)))
+    edz = lib.entropy_from_logits_bwd(d["z"], lse, H, d["grad"], T,
+                                      dlogits=_sentinel(N, torch.bfloat16, (N, V_)))
+    return H, lp, lse, sdz, edz
+
+
+def _check_entropy_selective(d, c, z64, ri, H, lp, lse, sdz, edz):
+    gs = d["grad"].index_select(0, ri).cpu().numpy()
+    lp_o, lse_o = oracle.selective_log_softmax(z64, c.ids, T)
+    H_o = oracle.entropy_from_logits(z64, T)
+    assert_rel(H.index_select(0, ri).cpu().numpy(), H_o, "entropy")
+    assert_rel(lp.index_select(0, ri).cpu().numpy(), lp_o, "selective logp")
+    assert_rel(lse.index_select(0, ri).cpu().numpy(), lse_o, "selective lse")
+    g64 = gs.astype(np.float64)
+    want = oracle.selective_log_softmax_bwd(z64, c.ids, g64, T)
+    assert_bf16_dz(dev_to_f64(sdz.index_select(0, ri)), want, "selective backward")
+    # the backwards take the library's lse and H, which carry the forwards'
+    # bars (asserted just above): their effect on dz_j = -(g/T) p_j (log p_j
+    # + H) is at most |g/T| p_j (d_lse (1 + |log p_j + H|) + d_H)
+    wantH = oracle.entropy_from_logits_bwd(z64, g64, T)
+    logp = z64 / T - lse_o[:, None]
+    p = np.exp(logp)
+    d_lse, d_H = 1e-5 * np.abs(lse_o) + 1e-6, 1e-5 * np.abs(H_o) + 1e-6
+    tolH = (1e-5 + 2.0 ** -8) * np.abs(wantH) + _entropy_bound(z64, T, gs, lse_o, H_o) + \
+        (np.abs(g64) / T)[:, None] * p * (d_lse[:, None] * (1 + np.abs(logp + H_o[:, None]))
+                                          + d_H[:, None]) + 1e-30
+    errH = np.abs(dev_to_f64(edz.index_select(0, ri)) - wantH)
+    assert (errH <= tolH).all(), f"entropy backward: max err {errH.max()}"
+    say("  entropy and selective log-softmax, forward and backward, match the oracle")
 
 
 def test_token_level_past_one_dispatch():
@@ -149,12 +188,7 @@ def test_token_level_past_one_dispatch():
         mask=d["mask"], dlogits=_sentinel(N, torch.bfloat16, (N, V)),
         zero_row=_sentinel(N, torch.uint8), err_count=err1,
         out=_grpo_outputs(N, B, "token", with_gathered=False), **kw)
-    H = lib.entropy_from_logits(d["z"], T, out=_sentinel(N))
-    lp, lse = lib.selective_log_softmax(d["z"], d["ids"], T, out=_sentinel(N), lse=_sentinel(N))
-    sdz = lib.selective_log_softmax_bwd(d["z"], d["ids"], lse, d["grad"], T,
-                                        dlogits=_sentinel(N, torch.bfloat16, (N, V)))
-    edz = lib.entropy_from_logits_bwd(d["z"], lse, H, d["grad"], T,
-                                      dlogits=_sentinel(N, torch.bfloat16, (N, V)))
+    H, lp, lse, sdz, edz = _entropy_selective(lib, d, N)
     torch.cuda.synchronize()
 
     for name, t in list(fwd.items()) + [("dz", dz), ("zero_row", zr)] + \
@@ -181,28 +215,7 @@ def test_token_level_past_one_dispatch():
         check_backward(c, o, g, dzx.index_select(0, ri), zrx.index_select(0, ri), z64, inp)
         say(f"  {what}: forward and backward match the oracle")
 
-    gs = d["grad"].index_select(0, ri).cpu().numpy()
-    lp_o, lse_o = oracle.selective_log_softmax(z64, c.ids, T)
-    H_o = oracle.entropy_from_logits(z64, T)
-    assert_rel(H.index_select(0, ri).cpu().numpy(), H_o, "entropy")
-    assert_rel(lp.index_select(0, ri).cpu().numpy(), lp_o, "selective logp")
-    assert_rel(lse.index_select(0, ri).cpu().numpy(), lse_o, "selective lse")
-    g64 = gs.astype(np.float64)
-    want = oracle.selective_log_softmax_bwd(z64, c.ids, g64, T)
-    assert_bf16_dz(dev_to_f64(sdz.index_select(0, ri)), want, "selective backward")
-    # the backwards take the library's lse and H, which carry the forwards'
-    # bars (asserted just above): their effect on dz_j = -(g/T) p_j (log p_j
-    # + H) is at most |g/T| p_j (d_lse (1 + |log p_j + H|) + d_H)
-    wantH = oracle.entropy_from_logits_bwd(z64, g64, T)
-    logp = z64 / T - lse_o[:, None]
-    p = np.exp(logp)
-    d_lse, d_H = 1e-5 * np.abs(lse_o) + 1e-6, 1e-5 * np.abs(H_o) + 1e-6
-    tolH = (1e-5 + 2.0 ** -8) * np.abs(wantH) + _entropy_bound(z64, T, gs, lse_o, H_o) + \
-        (np.abs(g64) / T)[:, None] * p * (d_lse[:, None] * (1 + np.abs(logp + H_o[:, None]))
-                                          + d_H[:, None]) + 1e-30
-    errH = np.abs(dev_to_f64(edz.index_select(0, ri)) - wantH)
-    assert (errH <= tolH).all(), f"entropy backward: max err {errH.max()}"
-    say("  entropy and selective log-softmax, forward and backward, match the oracle")
+    _check_entropy_selective(d, c, z64, ri, H, lp, lse, sdz, edz)
 
 
 def test_sequence_level_past_one_dispatch():
@@ -251,3 +264,57 @@ def test_sequence_level_past_one_dispatch():
     assert (ws[~m] == 0.0).all()
     assert (np.abs(ws * n_b * B - 1.0)[m] <= 2.0 ** -23).all()
     say("  forward, backward and the sequence-mean weights match the oracle")
+
+
+def test_longest_rows():
+    """Two rows of V = 2^26 bf16 (128 MB each), the longest the library
+    accepts: the forward streams each row with one 1024-lane workgroup, the
+    backward splits each into 16384 chunks of 512 vectors (the entropy
+    backward into 2048 of 4096), and the single pass, whose rows must fit in
+    registers, runs as forward then backward.  Row 0 samples the last column
+    and has weight 0 (a zero row over all of its chunks), row 1 the first."""
+    lib = require_gpu()
+    Vmax = 1 << 26
+    B, L = 2, 1
+    N = B * L
+    beta = 0.04
+    say(f"longest rows: {N} rows of V = 2^26 bf16 ({N * Vmax * 2 >> 20} MiB)")
+    d = _draw(B, L, seed=31, V=Vmax)
+    d["ids"][0], d["ids"][1] = Vmax - 1, 0
+    d["mask"][:] = 1
+    d["dloss"][:] = torch.tensor([0.0, 1.0], device="cuda")
+    d["grad"][:] = torch.tensor([0.0, 0.7], device="cuda")
+    kw = dict(temperature=T, beta=beta, eps_low=EPS_LOW, eps_high=EPS_HIGH)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fwd = lib.grpo_logits_fwd(d["z"], d["ids"], d["old"], d["adv"], B, L, ref_logp=d["ref"],
+                              mask=d["mask"], err_count=err, out=_grpo_outputs(N, B, "token"),
+                              **kw)
+    dz, zr = lib.grpo_logits_bwd(d["z"], d["ids"], d["old"], d["adv"], B, L, fwd["logp"],
+                                 fwd["lse"], d["dloss"], ref_logp=d["ref"], mask=d["mask"],
+                                 dlogits=_sentinel(N, torch.bfloat16, (N, Vmax)),
+                                 zero_row=_sentinel(N, torch.uint8), **kw)
+    err1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    one, dz1, zr1 = lib.grpo_logits_fwd_bwd(
+        d["z"], d["ids"], d["old"], d["adv"], B, L, d["dloss"], ref_logp=d["ref"],
+        mask=d["mask"], dlogits=_sentinel(N, torch.bfloat16, (N, Vmax)),
+        zero_row=_sentinel(N, torch.uint8), err_count=err1,
+        out=_grpo_outputs(N, B, "token", with_gathered=False), **kw)
+    H, lp, lse, sdz, edz = _entropy_selective(lib, d, N)
+    torch.cuda.synchronize()
+    for name, t in list(fwd.items()) + [("dz", dz), ("zero_row", zr)] + \
+            [(f"single {k}", v) for k, v in one.items()] + \
+            [("single dz", dz1), ("single zero_row", zr1), ("entropy", H), ("selective logp", lp),
+             ("selective lse", lse), ("selective dz", sdz), ("entropy dz", edz)]:
+        _all_written(name, t)
+    assert zr.tolist() == [1, 0] and zr1.tolist() == [1, 0]
+    assert int(err.item()) == 0 and int(err1.item()) == 0
+
+    c, inp, z64, ri, si = _sub_inputs(d, np.arange(B, dtype=np.int64), L, "token", beta)
+    for what, outs, dzx, zrx in (("two-pass", fwd, dz, zr), ("single pass", one, dz1, zr1)):
+        got = _pick(outs, ri, si)
+        got["err_count"] = err
+        o, g = oracle_expectations(inp, z64, got)
+        check_forward(c, o, got, ref=inp.ref)
+        check_backward(c, o, g, dzx, zrx, z64, inp)
+        say(f"  {what}: forward and backward match the oracle")
+    _check_entropy_selective(d, c, z64, ri, H, lp, lse, sdz, edz)
