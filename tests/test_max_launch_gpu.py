@@ -318,3 +318,66 @@ def test_longest_rows():
         check_backward(c, o, g, dzx, zrx, z64, inp)
         say(f"  {what}: forward and backward match the oracle")
     _check_entropy_selective(d, c, z64, ri, H, lp, lse, sdz, edz)
+
+
+def test_fused_chunk_past_one_dispatch():
+    """The chunked fused-linear loss on 16778216 one-token sequences (H = 64,
+    V = 8, every row weighted): the row gather (one 256-lane workgroup per
+    kept row) takes two launches, the boundary at compact row 16777215 (every
+    row is kept, so compact row i is row i).  grad_hidden of the rows around
+    the boundary, the first, the last and 16 drawn at random against the
+    oracle within the per-element bound of test_fused_gpu.py; every row of
+    grad_hidden written; loss and grad_weight finite."""
+    from test_fused_gpu import U, _assert_bound, _coef_error, _dz_error
+    lib = require_gpu()
+    H, Vf, beta = 64, 8, 0.04
+    R = BWD_STEP + 1001
+    say(f"fused chunk past one dispatch: {R} rows (one token each), H={H} V={Vf}; "
+        f"{-(-R // BWD_STEP)} gather launches")
+    g = torch.Generator(device="cuda").manual_seed(41)
+    dv = dict(device="cuda", generator=g)
+    lu = -math.log(Vf)
+    h = torch.randn(R, H, **dv).to(torch.bfloat16)
+    W = (torch.randn(Vf, H, **dv) * 0.25).to(torch.bfloat16)
+    ids = torch.randint(0, Vf, (R,), **dv)
+    old = lu + 0.3 * torch.randn(R, **dv)
+    ref = lu + 0.1 * torch.randn(R, **dv)
+    adv = torch.randn(R, **dv)
+    adv[::4] = 0.0
+    dloss = torch.ones(R, device="cuda")
+    gh = _sentinel(R * H).view(R, H)
+    loss, gh, gW = lib.fused_linear_grpo_chunk(h, W, ids, old, adv, None, dloss, R, 1,
+                                               ref_logp=ref, temperature=T, beta=beta,
+                                               eps_low=EPS_LOW, eps_high=EPS_HIGH,
+                                               grad_hidden=gh)
+    torch.cuda.synchronize()
+    _all_written("grad_hidden", gh)
+    assert bool(torch.isfinite(loss).all()) and bool(torch.isfinite(gW).all())
+
+    rng = np.random.default_rng(42)
+    rows = np.unique(np.concatenate([np.arange(BWD_STEP - 4, BWD_STEP + 4), [0, R - 1],
+                                     rng.integers(0, R, 16)])).astype(np.int64)
+    ri = torch.from_numpy(rows).cuda()
+    host = lambda t: t.index_select(0, ri).cpu().numpy()
+    hb = h.index_select(0, ri).view(torch.int16).cpu().numpy().view(np.uint16)
+    hs = oracle.decode_bf16(hb)
+    W64 = oracle.decode_bf16(W.view(torch.int16).cpu().numpy().view(np.uint16))
+    n = len(rows)
+    ids_s, old_s, ref_s = host(ids), host(old).astype(np.float64), host(ref).astype(np.float64)
+    adv_s, w_s = host(adv), host(dloss)
+    z = hs @ W64.T
+    fwd = oracle.grpo_forward(z, ids_s, old_s, ref_s, adv_s, None, n, 1, T, beta, EPS_LOW,
+                              EPS_HIGH)
+    gs = oracle.grpo_dlogp(fwd, ref_s, adv_s, None, w_s, n, 1, beta)
+    e_g = _coef_error(fwd["logp"], fwd["ratio"], fwd["is_clipped"],
+                      adv_s.astype(np.float64), ref_s, w_s.astype(np.float64), beta)
+    aW = np.abs(W64)
+    zeta = 2 * H * U * (np.abs(hs) @ aW.T)
+    onehot = np.zeros_like(z)
+    onehot[np.arange(n), ids_s] = 1.0
+    dz, E = _dz_error(z, zeta, fwd["lse"], gs, e_g, onehot, T)
+    want = dz @ W64
+    bound = E @ aW + 2 * (Vf + 1) * U * ((np.abs(dz) + E) @ aW)
+    worst = _assert_bound(host(gh), want, bound, "grad_hidden")
+    say(f"  {n} rows of grad_hidden around compact row {BWD_STEP} within the bound "
+        f"(largest error / bound {worst:.3f})")
