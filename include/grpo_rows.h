@@ -265,7 +265,8 @@ int selective_log_softmax_bwd(const void* logits, int dtype, int64_t rows, int64
  *   bytes), the per-row softmax statistics (8 R bytes per 128 columns of
  *   V, later reused for grad_hidden's split-K partial sums) and the
  *   compacted rows' hidden states and inputs (about 2 R H + 36 R).
- * H must be a multiple of 64 and at most 65536; V a multiple of 8.  hidden,
+ * H must be a multiple of 64 and at most 65536; V a multiple of 8 and at
+ * most 2^30; R = nseq * L at most 2^30 (GRPO_ERR_SHAPE otherwise).  hidden,
  * weight and grad_hidden 16-byte aligned.  The result is deterministic.
  * grad_weight's product runs on a stream the library keeps per device
  * (default priority, made on the first call), forked from and joined back
