@@ -57,6 +57,19 @@ def test_decode_bf16_hand_values():
     assert oracle.decode_bf16(pats).tolist() == want
 
 
+
+def test_to_f64_per_dtype():
+    """fp32 logits widen exactly (every float32 is a float64); bf16 logits
+    arrive as their bit patterns and come back as the values those patterns
+    stand for, checked here by hand, not through decode_bf16."""
+    f32 = np.array([[1.0, -2.5, 3.0e38, 1.0e-45], [0.1, -0.0, 7.0, 2.0 ** -20]], np.float32)
+    got = oracle.to_f64(f32, "f32")
+    assert got.dtype == np.float64 and got.shape == f32.shape
+    assert np.array_equal(got, f32.astype(np.float64)) and np.signbit(got[1, 1])
+    bits = np.array([[0x3F80, 0xC020], [0x4120, 0x0000]], np.uint16)   # 1, -2.5, 10, +0
+    assert oracle.to_f64(bits, "bf16").tolist() == [[1.0, -2.5], [10.0, 0.0]]
+
+
 # ---------------------------------------------------------------------------
 # library routines
 # ---------------------------------------------------------------------------
